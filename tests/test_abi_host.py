@@ -1,0 +1,181 @@
+"""Host-side checks of the C ABI: no GPU work is ever launched here.
+
+Every call below either fails validation (which happens before any HIP call)
+or has a zero extent (which returns without a launch), so fake pointers are
+never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from virtual_noise_perturbed_amd import _lib
+import virtual_noise_perturbed_amd as vn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vn.h")
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: every call with it must fail validation
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert "vn_perturbed_linear" in names and "vn_weight_gradient" in names
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in vn.h but not exported"
+    # and the binding knows every one of them
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_abi_version_and_status_strings(lib):
+    text = open(HEADER).read()
+    ver = int(re.search(r"#define VN_ABI_VERSION (\d+)", text).group(1))
+    assert lib.vn_abi_version() == ver
+    for code in range(8):
+        assert lib.vn_status_string(code).decode() not in ("", "unknown status")
+    assert lib.vn_status_string(99).decode() == "unknown status"
+
+
+def test_compute_offsets_page_example():
+    # page entry compute_offsets, its printed example
+    assert vn.compute_offsets([(256, 784), (256,), (10, 256), (10,)]) == [0, 200704, 200960, 203520]
+    assert vn.compute_offsets([(256, 784), (256,), (256, 256), (256,), (10, 256), (10,)]) == \
+        [0, 200704, 200960, 266496, 266752, 269312]
+    assert vn.compute_offsets([]) == []
+    assert vn.compute_offsets([(), (3,), (2, 2)]) == [0, 1, 4]
+
+
+def test_compute_offsets_errors(lib):
+    i64 = ctypes.c_int64
+    out = (i64 * 2)()
+    dims = (i64 * 2)(2**62, 2**62)
+    nd = (ctypes.c_int32 * 2)(1, 1)
+    assert lib.vn_compute_offsets(dims, nd, 2, out, None) == _lib.VN_ERR_OVERFLOW   # sum = 2^63
+    nd2 = (ctypes.c_int32 * 1)(2)
+    assert lib.vn_compute_offsets(dims, nd2, 1, out, None) == _lib.VN_ERR_OVERFLOW  # product = 2^124
+    dims = (i64 * 2)(3, -1)
+    assert lib.vn_compute_offsets(dims, nd, 2, out, None) == _lib.VN_ERR_SHAPE
+    assert lib.vn_compute_offsets(dims, nd, -1, out, None) == _lib.VN_ERR_SHAPE
+    assert lib.vn_compute_offsets(dims, None, 2, out, None) == _lib.VN_ERR_NULL
+    nd_bad = (ctypes.c_int32 * 2)(1, -2)
+    assert lib.vn_compute_offsets(dims, nd_bad, 2, out, None) == _lib.VN_ERR_SHAPE
+    assert lib.vn_compute_offsets(None, None, 0, None, None) == _lib.VN_OK
+    with pytest.raises(ValueError):
+        vn.compute_offsets([(2**40, 2**40)])
+
+
+def fwd(lib, **kw):
+    a = dict(x=FAKE, stride=0, w=FAKE, dtype=_lib.VN_F32, b=NULL, seeds=FAKE, sdt=_lib.VN_I64, pop=4,
+             batch=2, i=8, o=3, sigma=0.1, offset=0, act=0, y=FAKE, stream=NULL)
+    a.update(kw)
+    return lib.vn_perturbed_linear(a["x"], a["stride"], a["w"], a["dtype"], a["b"], a["seeds"], a["sdt"],
+                                   a["pop"], a["batch"], a["i"], a["o"], a["sigma"], a["offset"], a["act"],
+                                   a["y"], a["stream"])
+
+
+def test_forward_validation(lib):
+    E = _lib
+    assert fwd(lib, dtype=7) == E.VN_ERR_DTYPE
+    assert fwd(lib, sdt=5) == E.VN_ERR_DTYPE
+    assert fwd(lib, pop=-1) == E.VN_ERR_SHAPE
+    assert fwd(lib, batch=-1) == E.VN_ERR_SHAPE
+    assert fwd(lib, i=-1) == E.VN_ERR_SHAPE
+    assert fwd(lib, o=-1) == E.VN_ERR_SHAPE
+    assert fwd(lib, stride=5) == E.VN_ERR_SHAPE          # neither 0 nor batch*in
+    assert fwd(lib, sigma=float("nan")) == E.VN_ERR_VALUE
+    assert fwd(lib, sigma=float("inf")) == E.VN_ERR_VALUE
+    assert fwd(lib, offset=-1) == E.VN_ERR_VALUE
+    assert fwd(lib, act=9) == E.VN_ERR_VALUE
+    assert fwd(lib, offset=2**63 - 20) == E.VN_ERR_OVERFLOW   # offset + out*in + out > INT64_MAX
+    assert fwd(lib, o=2**40, i=2**40) == E.VN_ERR_OVERFLOW
+    assert fwd(lib, y=NULL) == E.VN_ERR_NULL
+    assert fwd(lib, seeds=NULL) == E.VN_ERR_NULL
+    assert fwd(lib, x=NULL) == E.VN_ERR_NULL
+    assert fwd(lib, w=NULL) == E.VN_ERR_NULL
+    assert fwd(lib, y=ctypes.c_void_p(0x10002)) == E.VN_ERR_ALIGN
+    assert fwd(lib, seeds=ctypes.c_void_p(0x10004)) == E.VN_ERR_ALIGN
+    assert fwd(lib, x=ctypes.c_void_p(0x10002)) == E.VN_ERR_ALIGN
+    # zero extents: nothing to do, nothing launched, even with NULL outputs
+    assert fwd(lib, pop=0, y=NULL, x=NULL, w=NULL, seeds=NULL) == E.VN_OK
+    assert fwd(lib, batch=0, y=NULL) == E.VN_OK
+    assert fwd(lib, o=0, y=NULL) == E.VN_OK
+
+
+def grad(lib, fn, **kw):
+    a = dict(f=FAKE, seeds=FAKE, sdt=_lib.VN_I64, pop=4, n=6, sigma=0.1, offset=0, out=FAKE)
+    a.update(kw)
+    if fn == "flat":
+        return lib.vn_flat_gradient(a["f"], a["seeds"], a["sdt"], a["pop"], a["n"], a["sigma"], a["offset"],
+                                    a["out"], None)
+    if fn == "bias":
+        return lib.vn_bias_gradient(a["f"], a["seeds"], a["sdt"], a["pop"], a["n"], a["sigma"], a["offset"],
+                                    a["out"], None)
+    return lib.vn_weight_gradient(a["f"], a["seeds"], a["sdt"], a["pop"], a["n"], 3, a["sigma"], a["offset"],
+                                  a["out"], None)
+
+
+@pytest.mark.parametrize("fn", ["flat", "bias", "weight"])
+def test_gradient_validation(lib, fn):
+    E = _lib
+    assert grad(lib, fn, sdt=3) == E.VN_ERR_DTYPE
+    assert grad(lib, fn, n=-1) == E.VN_ERR_SHAPE
+    assert grad(lib, fn, pop=0) == E.VN_ERR_VALUE
+    assert grad(lib, fn, pop=-3) == E.VN_ERR_VALUE
+    assert grad(lib, fn, sigma=0.0) == E.VN_ERR_VALUE      # the estimator divides by sigma
+    assert grad(lib, fn, sigma=float("nan")) == E.VN_ERR_VALUE
+    assert grad(lib, fn, sigma=1e-45) == E.VN_ERR_VALUE    # 1/(pop*sigma) overflows fp32
+    assert grad(lib, fn, offset=-5) == E.VN_ERR_VALUE
+    assert grad(lib, fn, offset=2**63 - 2) == E.VN_ERR_OVERFLOW
+    assert grad(lib, fn, f=NULL) == E.VN_ERR_NULL
+    assert grad(lib, fn, seeds=NULL) == E.VN_ERR_NULL
+    assert grad(lib, fn, out=NULL) == E.VN_ERR_NULL
+    assert grad(lib, fn, out=ctypes.c_void_p(0x10001)) == E.VN_ERR_ALIGN
+    assert grad(lib, fn, n=0, out=NULL) == E.VN_OK
+
+
+def test_metric_and_noise_validation(lib):
+    E = _lib
+    m = lambda **kw: lib.vn_reduce_metric(kw.get("c", FAKE), kw.get("s", FAKE), kw.get("sdt", 0),
+                                          kw.get("pop", 3), kw.get("n", 5), kw.get("sigma", 0.1),
+                                          kw.get("offset", 0), kw.get("out", FAKE), None)
+    assert m(sdt=4) == E.VN_ERR_DTYPE
+    assert m(pop=-1) == E.VN_ERR_SHAPE
+    assert m(n=0) == E.VN_ERR_SHAPE
+    assert m(sigma=float("inf")) == E.VN_ERR_VALUE
+    assert m(offset=-1) == E.VN_ERR_VALUE
+    assert m(c=NULL) == E.VN_ERR_NULL
+    assert m(pop=0, c=NULL, out=NULL) == E.VN_OK
+    nz = lambda **kw: lib.vn_noise_u32(kw.get("s", FAKE), kw.get("sdt", 0), kw.get("pop", 2), kw.get("n", 4),
+                                       kw.get("offset", 0), kw.get("out", FAKE), None)
+    assert nz(sdt=2) == E.VN_ERR_DTYPE
+    assert nz(n=-4) == E.VN_ERR_SHAPE
+    assert nz(offset=-4) == E.VN_ERR_VALUE
+    assert nz(out=NULL) == E.VN_ERR_NULL
+    assert nz(s=ctypes.c_void_p(0x10004)) == E.VN_ERR_ALIGN
+    assert nz(n=0, out=NULL) == E.VN_OK
+    assert lib.vn_noise_f32(FAKE, 0, 2, 4, 2**63 - 1, FAKE, None) == E.VN_ERR_OVERFLOW
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(2, 3)
+    w = torch.zeros(4, 3)
+    s = torch.arange(2)
+    with pytest.raises(ValueError, match="GPU"):
+        vn.virtual_perturbed_linear(x, w, None, s, 0.1, 0)
+    with pytest.raises(ValueError, match="GPU"):
+        vn.virtual_weight_gradient(torch.zeros(2), s, (4, 3), 0.1, 2, 0)

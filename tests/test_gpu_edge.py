@@ -1,0 +1,137 @@
+"""Ragged shapes, every kernel variant, degenerate sizes and the reduce metric,
+each against the full CPU oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import virtual_noise_perturbed_amd as vn
+import workloads
+from gpu_util import TOL_BF16, TOL_F32, assert_close, device, sigma32, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# (pop, batch, in, out, dtype, bias, shared_x, offset)
+CASES = [
+    (3, 5, 13, 10, "f32", True, False, 0),          # in not a multiple of 4: scalar loads
+    (7, 33, 784, 10, "f32", True, False, 200960),   # rows 33 -> two 32-row blocks, out 10
+    (5, 1, 7, 300, "f32", False, False, 3),         # batch 1, in below one k-chunk
+    (2, 300, 70, 40, "f32", True, False, 11),       # batch > 256: two row tiles
+    (4, 64, 256, 256, "f32", True, True, 2**40),    # shared x, huge offset
+    (6, 100, 96, 129, "f32", True, False, 5),       # 128-row variant, ragged out
+    (3, 200, 64, 65, "f32", False, False, 0),       # 256-row variant
+    (3, 5, 24, 10, "bf16", True, False, 0),
+    (4, 32, 136, 70, "bf16", False, False, 9),
+    (2, 64, 1000, 33, "bf16", True, True, 1 << 33),
+    (3, 130, 72, 50, "bf16", True, False, 4),
+    (2, 260, 48, 20, "bf16", False, False, 1),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[4]}-p{c[0]}b{c[1]}i{c[2]}o{c[3]}{'-shared' if c[6] else ''}"
+                                             for c in CASES])
+def test_ragged_forward(case):
+    pop, batch, fin, fout, dt, bias, shared, offset = case
+    print(f"ragged forward {case}", flush=True)
+    wl = workloads.make_custom(pop, batch, fin, fout, dtype=dt, bias=bias, shared_x=shared, sigma=0.05,
+                               offset=offset, seed=fin + fout, seed_base=-2)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    L = wl.layers[0]
+    y = vn.virtual_perturbed_linear(to_dev(wl.x, tdt), to_dev(L.weight, tdt),
+                                    None if L.bias is None else to_dev(L.bias), to_dev(wl.seeds),
+                                    wl.sigma, offset).cpu().numpy()
+    ref = oracle.perturbed_linear(wl.x, L.weight, L.bias, wl.seeds, sigma32(wl.sigma), offset)
+    assert_close(y, ref, TOL_BF16 if dt == "bf16" else TOL_F32, str(case))
+
+
+def test_misaligned_base_pointer_path():
+    """in a multiple of 4 but x not 16-byte aligned: the kernel takes element loads."""
+    dev = device()
+    pop, batch, fin, fout = 3, 8, 32, 24
+    wl = workloads.make_custom(pop, batch, fin, fout, seed=3)
+    L = wl.layers[0]
+    buf = torch.empty(pop * batch * fin + 1, device=dev)
+    x = buf[1:].view(pop, batch, fin)
+    x.copy_(to_dev(wl.x))
+    assert x.data_ptr() % 16 != 0
+    y = vn.virtual_perturbed_linear(x, to_dev(L.weight), to_dev(L.bias), to_dev(wl.seeds), wl.sigma, 0)
+    ref = oracle.perturbed_linear(wl.x, L.weight, L.bias, wl.seeds, sigma32(wl.sigma), 0)
+    assert_close(y.cpu().numpy(), ref, TOL_F32, "misaligned x")
+
+
+def test_relu_int32_seeds():
+    pop, batch, fin, fout = 5, 20, 40, 30
+    wl = workloads.make_custom(pop, batch, fin, fout, seed=9, seed_base=-100)
+    L = wl.layers[0]
+    s32 = to_dev(wl.seeds.astype(np.int32))
+    y = vn.virtual_perturbed_linear(to_dev(wl.x), to_dev(L.weight), to_dev(L.bias), s32, wl.sigma, 17,
+                                    activation="relu").cpu().numpy()
+    ref = np.maximum(oracle.perturbed_linear(wl.x, L.weight, L.bias, wl.seeds, sigma32(wl.sigma), 17), 0)
+    assert_close(y, ref, TOL_F32, "relu / int32 seeds")
+    assert (y >= 0).all()
+
+
+def test_sigma_zero_is_plain_linear():
+    pop, batch, fin, fout = 4, 9, 50, 20
+    wl = workloads.make_custom(pop, batch, fin, fout, seed=10)
+    L = wl.layers[0]
+    y = vn.virtual_perturbed_linear(to_dev(wl.x), to_dev(L.weight), to_dev(L.bias), to_dev(wl.seeds), 0.0, 0)
+    ref = np.einsum("pbk,jk->pbj", wl.x.astype(np.float64), L.weight.astype(np.float64)) + L.bias
+    assert_close(y.cpu().numpy(), ref, TOL_F32, "sigma 0")
+
+
+def test_degenerate_sizes():
+    dev = device()
+    s = to_dev(np.arange(3, dtype=np.int64))
+    # in = 0: only the bias term remains (b + sigma nb)
+    b = torch.ones(5, device=dev)
+    y = vn.virtual_perturbed_linear(torch.empty((3, 2, 0), device=dev), torch.empty((5, 0), device=dev), b,
+                                    s, 0.5, 7).cpu().numpy()
+    nb = oracle.noise(np.arange(3), 5, 7)
+    assert_close(y, np.broadcast_to((1 + np.float64(np.float32(0.5)) * nb)[:, None, :], (3, 2, 5)), TOL_F32, "in=0")
+    # empty population / batch / out
+    assert vn.virtual_perturbed_linear(torch.zeros((0, 2, 4), device=dev), torch.zeros((3, 4), device=dev), None,
+                                       torch.zeros(0, dtype=torch.int64, device=dev), 0.1, 0).shape == (0, 2, 3)
+    assert vn.virtual_perturbed_linear(torch.zeros((0, 4), device=dev), torch.zeros((3, 4), device=dev), None,
+                                       s, 0.1, 0).shape == (3, 0, 3)
+    assert vn.virtual_perturbed_linear(torch.zeros((2, 4), device=dev), torch.zeros((0, 4), device=dev), None,
+                                       s, 0.1, 0).shape == (3, 2, 0)
+    f = torch.ones(3, device=dev)
+    assert vn.virtual_weight_gradient(f, s, (0, 4), 0.1, 3, 0).shape == (0, 4)
+    # pop 1, one element
+    g = vn.virtual_flat_gradient(torch.tensor([2.0], device=dev), s[:1], 1, 0.25, 1, 123).cpu().numpy()
+    assert_close(g, oracle.weight_gradient_at(np.array([2.0]), np.array([0]), 0.25, 1, 123, [0]), TOL_F32, "1x1")
+
+
+@pytest.mark.parametrize("pop,n", [(1, 5), (63, 1000), (64, 16384), (65, 16385), (1000, 3000), (3, 70001)])
+def test_gradient_shapes(pop, n):
+    print(f"gradient pop={pop} n={n}", flush=True)
+    rng = np.random.default_rng(pop + n)
+    seeds = rng.integers(-2**62, 2**62, size=pop)
+    fit = rng.standard_normal(pop).astype(np.float32)
+    sig = 0.03
+    g = vn.virtual_flat_gradient(to_dev(fit), to_dev(seeds), n, sig, pop, 999).cpu().numpy()
+    idx = np.unique(np.concatenate([np.arange(min(n, 50)), n - 1 - np.arange(min(n, 50)), rng.integers(0, n, 500)]))
+    ref = oracle.weight_gradient_at(fit.astype(np.float64), seeds, sigma32(sig), pop, 999, idx)
+    assert_close(g[idx], ref, TOL_F32, f"pop {pop} n {n}")
+
+
+def test_binding_checks_pop_size():
+    dev = device()
+    s = to_dev(np.arange(4, dtype=np.int64))
+    with pytest.raises(ValueError):
+        vn.virtual_weight_gradient(torch.ones(4, device=dev), s, (2, 3), 0.1, 5, 0)
+    with pytest.raises(ValueError):
+        vn.virtual_weight_gradient(torch.ones(4, device=dev), s, (2, 3), 0.0, 4, 0)
+
+
+@pytest.mark.parametrize("pop,n,offset", [(6, 1000, 0), (3, 269322, 5), (1, 1, 2**35), (40, 4097, 77)])
+def test_reduce_metric(pop, n, offset):
+    rng = np.random.default_rng(n)
+    center = rng.standard_normal(n).astype(np.float32)
+    seeds = np.arange(pop, dtype=np.int64) * 31 - 7
+    sig = 0.3
+    got = vn.virtual_reduce_metric(to_dev(center), to_dev(seeds), sig, n, offset).cpu().numpy()
+    ref = oracle.reduce_metric(center, seeds, sigma32(sig), n, offset)
+    assert_close(got, ref, TOL_F32, "reduce metric")

@@ -1,0 +1,463 @@
+// HIP kernels of the virtual-noise ES linear layer for gfx950 (MI355X).
+//
+// Method: EvoX API page "evox.triton_kernels.kernels.virtual_noise" -- module
+// introduction (model and gradient equations), section "Noise indexing
+// scheme", API entries virtual_perturbed_linear, virtual_weight_gradient,
+// virtual_bias_gradient and virtual_reduce_metric.  The noise generator itself
+// lives in vn_device.hpp.
+//
+// Design notes (gfx950):
+//  * The hash (two 64-bit multiplies per element, built from 32-bit integer
+//    multiplies) is the dominant cost of every entry point, so each noise
+//    element is generated exactly once per (individual, element) and every
+//    kernel is organised around keeping the vector ALUs busy with it.
+//  * Forward: one workgroup (4 waves) per (individual, column tile).  Each wave
+//    owns NB column blocks and ALL rows of its individual's batch, so the noise
+//    it generates for a weight element is reused by every batch row through
+//    the matrix cores.  The perturbed weights W + sigma*N are generated directly
+//    in the MFMA B-operand layout in VGPRs and never touch LDS or HBM.  The sum
+//    over k is order-free, so each lane is given a contiguous run of k for its
+//    column: consecutive noise indices differ by +GAMMA in the state (one 64-bit
+//    add per element) and the W and X loads are 16-byte vectors.  X rows are
+//    read straight from global memory in the matching A-operand layout; the 4
+//    waves of a workgroup read the same rows, which the L1/L2 caches serve.
+//  * Gradients: element-major (lanes own consecutive elements, the population is
+//    walked with wave-uniform scalar loads of seed and fitness, split over the 4
+//    waves and reduced through LDS in a fixed order) for large blocks;
+//    population-major (lanes own individuals, one wave per element, fixed
+//    butterfly reduction) for small blocks such as biases.
+//  * No atomics anywhere: every output is a fixed-order reduction, so repeated
+//    calls are bit-identical.
+//  * Workgroup ids are remapped so that consecutive logical tiles (the column
+//    tiles of one individual, which share its X rows) land on the same XCD and
+//    its L2, given that the hardware deals workgroups round-robin over 8 XCDs.
+
+#include "vn_device.hpp"
+#include "vn_launch.hpp"
+
+namespace vn {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kXcds = 8;
+
+// Bijection on [0, n): hardware block b runs on XCD b % 8; give each XCD a
+// contiguous range of logical ids.
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t n) {
+  const int64_t per = n / kXcds, rem = n % kXcds;
+  const int64_t x = b % kXcds, local = b / kXcds;
+  return (x < rem) ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA shapes.  For every shape below the A operand of lane l holds row
+// (l % DIM) and the B operand holds column (l % DIM), both at the same k-slots
+// selected by (l / DIM); the kernels rely only on that symmetry and on the
+// output layout given by row_base() and row_off().
+template <typename DT, int DIM> struct Mfma;
+
+// Output element v of lane l sits at column l % DIM and row
+// row_base(l) + row_off(v).
+struct Out32 {
+  static constexpr int NACC = 16;
+  static __device__ __forceinline__ int row_base(int lane) { return 4 * (lane >> 5); }
+  static constexpr int row_off(int v) { return 8 * (v >> 2) + (v & 3); }
+};
+struct Out16 {
+  static constexpr int NACC = 4;
+  static __device__ __forceinline__ int row_base(int lane) { return 4 * (lane >> 4); }
+  static constexpr int row_off(int v) { return v; }
+};
+template <> struct Mfma<float, 32> : Out32 {   // v_mfma_f32_32x32x2_f32
+  static constexpr int KPL = 1, H = 2;
+  using Acc = f32x16;
+};
+template <> struct Mfma<float, 16> : Out16 {   // v_mfma_f32_16x16x4_f32
+  static constexpr int KPL = 1, H = 4;
+  using Acc = f32x4;
+};
+template <> struct Mfma<__bf16, 32> : Out32 {  // v_mfma_f32_32x32x16_bf16
+  static constexpr int KPL = 8, H = 2;
+  using Acc = f32x16;
+};
+template <> struct Mfma<__bf16, 16> : Out16 {  // v_mfma_f32_16x16x32_bf16
+  static constexpr int KPL = 8, H = 4;
+  using Acc = f32x4;
+};
+
+template <int DIM>
+__device__ __forceinline__ typename Mfma<float, DIM>::Acc mfma_f32(float a, float b, typename Mfma<float, DIM>::Acc c) {
+  if constexpr (DIM == 32) return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+template <int DIM>
+__device__ __forceinline__ typename Mfma<__bf16, DIM>::Acc mfma_bf16(bf16x8 a, bf16x8 b, typename Mfma<__bf16, DIM>::Acc c) {
+  if constexpr (DIM == 32) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(__bf16 v) { return static_cast<float>(v); }
+
+template <typename DT> __device__ __forceinline__ DT zero_of() { return static_cast<DT>(0.0f); }
+
+// R contiguous elements at p.  VEC: p is 16-byte aligned (checked on the host).
+template <typename DT, int R, bool VEC>
+__device__ __forceinline__ void load_run(DT (&dst)[R], const DT* p) {
+  if constexpr (VEC) {
+    constexpr int PER = 16 / sizeof(DT);
+    static_assert(R % PER == 0, "run must be whole 16-byte vectors");
+#pragma unroll
+    for (int q = 0; q < R / PER; ++q) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p + q * PER);
+      __builtin_memcpy(&dst[q * PER], &v, 16);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < R; ++t) dst[t] = p[t];
+  }
+}
+
+// First `valid` elements at p, zeros after (valid may be <= 0 or >= R).
+template <typename DT, int R>
+__device__ __forceinline__ void load_run_guarded(DT (&dst)[R], const DT* p, int valid) {
+#pragma unroll
+  for (int t = 0; t < R; ++t) dst[t] = (t < valid) ? p[t] : zero_of<DT>();
+}
+
+// ---------------------------------------------------------------------------
+// Forward: Y[i] = X[i] (W + sigma N_i)^T + (b + sigma nb_i)
+//
+// DT   operand type (float or __bf16)
+// DIM  MFMA block edge (32 or 16)
+// MB   row blocks per wave (the wave covers MB*DIM batch rows)
+// NB   column blocks per wave (the workgroup covers 4*NB*DIM columns)
+// T    MFMAs per k-chunk; each lane holds a run of R = T*KPL contiguous k
+template <typename DT, int DIM, int MB, int NB, int T, int WAVES, bool VEC>
+__global__ __launch_bounds__(256, WAVES) void forward_kernel(FwdParams p, int64_t n_tiles) {
+  using MF = Mfma<DT, DIM>;
+  using Acc = typename MF::Acc;
+  constexpr int R = T * MF::KPL;
+  constexpr int KC = MF::H * R;
+  constexpr int NT = 4 * NB * DIM;
+  constexpr uint64_t kChunkStep = gamma_times(KC);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ln = lane % DIM;   // row (A) / column (B) inside a block
+  const int lh = lane / DIM;   // k-slot group
+
+  const int64_t in = p.in, out = p.out, batch = p.batch;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * (MB * DIM);
+  const int64_t nfull = in / KC;
+  const int rem = static_cast<int>(in - nfull * KC);
+
+  {
+    const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t i = L / n_tiles;
+    const int64_t tile = L - i * n_tiles;
+
+    const uint64_t s = load_seed(p.seeds, p.seeds_i32, i);
+    const DT* __restrict__ xi = static_cast<const DT*>(p.x) + i * p.x_pop_stride;
+    const DT* __restrict__ w = static_cast<const DT*>(p.w);
+
+    const int64_t jbase = tile * NT + wave * (NB * DIM);
+    const DT* wrow[NB];
+    uint64_t z[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      int64_t j = jbase + nb * DIM + ln;
+      j = j < out ? j : out - 1;   // columns past `out` only feed discarded outputs
+      wrow[nb] = w + j * in + lh * R;
+      z[nb] = state_of(s, static_cast<uint64_t>(p.offset + j * in + lh * R));
+    }
+    const DT* xrow[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      int64_t b = m0 + mb * DIM + ln;
+      b = b < batch ? b : batch - 1;  // rows past `batch` only feed discarded outputs
+      xrow[mb] = xi + b * in + lh * R;
+    }
+
+    Acc acc[MB][NB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = Acc{};
+
+    // One k-chunk: for each column block, generate the lane's run of perturbed
+    // weights and feed it straight to the matrix cores (one block at a time
+    // keeps the live noise state small).
+    auto chunk = [&](const DT (&wv)[NB][R], const DT (&xv)[MB][R], int valid) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        float wp[R];
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+          const float nz = noise_of_state(z[nb] + gamma_times(t));
+          const float v = __builtin_fmaf(p.sigma, nz, to_f32(wv[nb][t]));
+          wp[t] = (t < valid) ? v : 0.0f;
+        }
+        z[nb] += kChunkStep;
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+          if constexpr (sizeof(DT) == 4) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mfma_f32<DIM>(xv[mb][tt], wp[tt], acc[mb][nb]);
+          } else {
+            bf16x8 bq;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bq[e] = static_cast<__bf16>(wp[tt * 8 + e]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+              bf16x8 a;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) a[e] = xv[mb][tt * 8 + e];
+              acc[mb][nb] = mfma_bf16<DIM>(a, bq, acc[mb][nb]);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    for (int64_t c = 0; c < nfull; ++c) {
+      DT wv[NB][R], xv[MB][R];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) load_run<DT, R, VEC>(wv[nb], wrow[nb] + c * KC);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) load_run<DT, R, VEC>(xv[mb], xrow[mb] + c * KC);
+      chunk(wv, xv, R);
+    }
+    if (rem > 0) {
+      const int valid = rem - lh * R;
+      DT wv[NB][R], xv[MB][R];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) load_run_guarded<DT, R>(wv[nb], wrow[nb] + nfull * KC, valid);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) load_run_guarded<DT, R>(xv[mb], xrow[mb] + nfull * KC, valid);
+      chunk(wv, xv, valid);
+    }
+
+    // Epilogue: bias b_j + sigma nb_i[j] with nb at offset + out*in + j.
+    const int rb = MF::row_base(lane);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int64_t j = jbase + nb * DIM + ln;
+      if (j >= out) continue;
+      float bj = 0.0f;
+      if (p.bias != nullptr) {
+        const float nz = noise_of_state(state_of(s, static_cast<uint64_t>(p.offset + out * in + j)));
+        bj = __builtin_fmaf(p.sigma, nz, p.bias[j]);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int64_t row0 = m0 + mb * DIM + rb;
+        float* __restrict__ yp = p.y + (i * batch + row0) * out + j;
+#pragma unroll
+        for (int v = 0; v < MF::NACC; ++v) {
+          const int ro = MF::row_off(v);
+          if (row0 + ro < batch) {
+            float val = acc[mb][nb][v] + bj;
+            if (p.relu) val = val > 0.0f ? val : 0.0f;
+            yp[static_cast<int64_t>(ro) * out] = val;
+          }
+        }
+      }
+    }
+  }
+}
+
+// WAVES: waves per SIMD the register allocation must allow.
+template <typename DT, int DIM, int MB, int NB, int T, int WAVES>
+static hipError_t launch_fwd_cfg(const FwdParams& p, hipStream_t stream) {
+  constexpr int NT = 4 * NB * DIM;
+  constexpr int ROWS = MB * DIM;
+  constexpr int R = T * Mfma<DT, DIM>::KPL;
+  const int64_t n_tiles = (p.out + NT - 1) / NT;
+  const int64_t total = p.pop * n_tiles;
+  const int64_t m_tiles = (p.batch + ROWS - 1) / ROWS;
+  if (total > kMaxGridX || m_tiles > 65535) return hipErrorInvalidConfiguration;
+  dim3 grid(static_cast<unsigned>(total), static_cast<unsigned>(m_tiles));
+  // 16-byte vector loads need every lane's run start to be 16-byte aligned:
+  // base pointers aligned, row length and pop stride multiples of 16 bytes.
+  const int64_t per = 16 / static_cast<int64_t>(sizeof(DT));
+  const bool vec = (reinterpret_cast<uintptr_t>(p.x) % 16 == 0) && (reinterpret_cast<uintptr_t>(p.w) % 16 == 0) &&
+                   (p.in % per == 0) && (p.x_pop_stride % per == 0) && (R % per == 0);
+  if (vec)
+    forward_kernel<DT, DIM, MB, NB, T, WAVES, true><<<grid, 256, 0, stream>>>(p, n_tiles);
+  else
+    forward_kernel<DT, DIM, MB, NB, T, WAVES, false><<<grid, 256, 0, stream>>>(p, n_tiles);
+  return hipGetLastError();
+}
+
+// Tile choice by batch size.  Each wave holds all rows of its individual in
+// MB row blocks, so every noise element is generated once per individual.
+template <typename DT, int T16, int T32, int TBIG>
+static hipError_t launch_fwd_dtype(const FwdParams& p, hipStream_t stream) {
+  if (p.batch <= 16) return launch_fwd_cfg<DT, 16, 1, 2, T16, 2>(p, stream);
+  if (p.batch <= 32) return launch_fwd_cfg<DT, 32, 1, 2, T32, 2>(p, stream);
+  if (p.batch <= 64) return launch_fwd_cfg<DT, 32, 2, 2, T32, 2>(p, stream);
+  if (p.batch <= 128) return launch_fwd_cfg<DT, 32, 4, 1, TBIG, 2>(p, stream);
+  // 256 rows per workgroup; larger batches take several row tiles (grid.y),
+  // each regenerating the same noise.
+  return launch_fwd_cfg<DT, 32, 8, 1, TBIG, 2>(p, stream);
+}
+
+hipError_t launch_forward_f32(const FwdParams& p, hipStream_t stream) {
+  return launch_fwd_dtype<float, 4, 8, 4>(p, stream);
+}
+hipError_t launch_forward_bf16(const FwdParams& p, hipStream_t stream) {
+  return launch_fwd_dtype<__bf16, 2, 2, 1>(p, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Gradient, element-major: grad[t] = scale * sum_i f_i noise_i[offset + t].
+// Lane owns E consecutive elements; wave w walks its quarter of the population.
+template <int E>
+__global__ __launch_bounds__(256) void grad_elem_kernel(GradParams p, int64_t n_blocks) {
+  __shared__ float red[4][64 * E];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t q = p.pop / 4, r = p.pop % 4;
+  const int64_t i_begin = wave * q + (wave < r ? wave : r);
+  const int64_t i_end = i_begin + q + (wave < r ? 1 : 0);
+
+  for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
+    const int64_t e0 = blk * (64 * E) + lane * E;
+    uint64_t c[E];
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      int64_t t = e0 + e;
+      t = t < p.n ? t : p.n - 1;
+      c[e] = state_of(0, static_cast<uint64_t>(p.offset + t));
+      acc[e] = 0.0f;
+    }
+    int64_t i = i_begin;
+    for (; i + 4 <= i_end; i += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint64_t s = load_seed(p.seeds, p.seeds_i32, i + u);
+        const float f = p.fitness[i + u];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(f, noise_of_state(s + c[e]), acc[e]);
+      }
+    }
+    for (; i < i_end; ++i) {
+      const uint64_t s = load_seed(p.seeds, p.seeds_i32, i);
+      const float f = p.fitness[i];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(f, noise_of_state(s + c[e]), acc[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) red[wave][lane * E + e] = acc[e];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int k = lane * E + e;
+        const float v = ((red[0][k] + red[1][k]) + red[2][k]) + red[3][k];
+        if (e0 + e < p.n) p.out[e0 + e] = v * p.scale;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Gradient, population-major: one wave per element, lanes own individuals.
+__global__ __launch_bounds__(256) void grad_pop_kernel(GradParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave_id = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t n_waves = static_cast<int64_t>(gridDim.x) * 4;
+  for (int64_t t = wave_id; t < p.n; t += n_waves) {
+    const uint64_t c = state_of(0, static_cast<uint64_t>(p.offset + t));
+    float acc = 0.0f;
+    for (int64_t i = lane; i < p.pop; i += 64)
+      acc = __builtin_fmaf(p.fitness[i], noise_of_state(load_seed(p.seeds, p.seeds_i32, i) + c), acc);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, 64);
+    if (lane == 0) p.out[t] = acc * p.scale;
+  }
+}
+
+hipError_t launch_gradient(const GradParams& p, hipStream_t stream) {
+  if (p.n <= 16384) {
+    const int64_t waves = p.n;
+    int64_t blocks = (waves + 3) / 4;
+    blocks = blocks < 65536 ? blocks : 65536;
+    grad_pop_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(p);
+  } else if (p.n < (int64_t(1) << 20)) {
+    const int64_t n_blocks = (p.n + 63) / 64;
+    const int64_t g = n_blocks < kMaxGridX ? n_blocks : kMaxGridX;
+    grad_elem_kernel<1><<<static_cast<unsigned>(g), 256, 0, stream>>>(p, n_blocks);
+  } else {
+    const int64_t n_blocks = (p.n + 255) / 256;
+    const int64_t g = n_blocks < kMaxGridX ? n_blocks : kMaxGridX;
+    grad_elem_kernel<4><<<static_cast<unsigned>(g), 256, 0, stream>>>(p, n_blocks);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Noise readout: r[i, t] and/or N[i, t] for indices offset + t.
+__global__ __launch_bounds__(256) void noise_kernel(const void* seeds, bool seeds_i32, int64_t pop, int64_t n,
+                                                    int64_t offset, uint32_t* r_out, float* n_out) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t i = blockIdx.y; i < pop; i += gridDim.y) {
+    const uint64_t s = load_seed(seeds, seeds_i32, i);
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; t < n; t += stride) {
+      const uint32_t r = mix_lo32(state_of(s, static_cast<uint64_t>(offset + t)));
+      if (r_out) r_out[i * n + t] = r;
+      if (n_out) n_out[i * n + t] = noise_of_bits(r);
+    }
+  }
+}
+
+hipError_t launch_noise(const void* seeds, bool seeds_i32, int64_t pop, int64_t n, int64_t offset,
+                        uint32_t* r_out, float* n_out, hipStream_t stream) {
+  int64_t gx = (n + 255) / 256;
+  gx = gx < 4096 ? gx : 4096;
+  const int64_t gy = pop < 65535 ? pop : 65535;
+  noise_kernel<<<dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)), 256, 0, stream>>>(
+      seeds, seeds_i32, pop, n, offset, r_out, n_out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Reduce metric: out[i] = mean_k |center[k] + sigma noise_i[offset + k]|.
+__global__ __launch_bounds__(256) void metric_kernel(const float* center, const void* seeds, bool seeds_i32,
+                                                     int64_t pop, int64_t n, float sigma, int64_t offset,
+                                                     float* out) {
+  __shared__ float red[256];
+  const int tid = threadIdx.x;
+  for (int64_t i = blockIdx.x; i < pop; i += gridDim.x) {
+    const uint64_t s = load_seed(seeds, seeds_i32, i);
+    uint64_t z = state_of(s, static_cast<uint64_t>(offset + tid));
+    float acc = 0.0f;
+    for (int64_t k = tid; k < n; k += 256) {
+      acc += __builtin_fabsf(__builtin_fmaf(sigma, noise_of_state(z), center[k]));
+      z += gamma_times(256);
+    }
+    red[tid] = acc;
+    __syncthreads();
+#pragma unroll
+    for (int h = 128; h >= 1; h >>= 1) {
+      if (tid < h) red[tid] += red[tid + h];
+      __syncthreads();
+    }
+    if (tid == 0) out[i] = red[0] / static_cast<float>(n);
+    __syncthreads();
+  }
+}
+
+hipError_t launch_reduce_metric(const float* center, const void* seeds, bool seeds_i32, int64_t pop, int64_t n,
+                                float sigma, int64_t offset, float* out, hipStream_t stream) {
+  const int64_t g = pop < 65536 ? pop : 65536;
+  metric_kernel<<<static_cast<unsigned>(g), 256, 0, stream>>>(center, seeds, seeds_i32, pop, n, sigma, offset, out);
+  return hipGetLastError();
+}
+
+}  // namespace vn

@@ -1,0 +1,48 @@
+// Internal launch interface between the C ABI (vn_api.cpp) and the kernels
+// (vn_kernels.hip).  Arguments reaching these functions are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vn {
+
+struct FwdParams {
+  const void* x;
+  int64_t x_pop_stride;  // elements between individuals' inputs (0 = shared)
+  const void* w;
+  const float* bias;     // may be null
+  const void* seeds;
+  bool seeds_i32;
+  int64_t pop, batch, in, out;
+  float sigma;
+  int64_t offset;
+  bool relu;
+  float* y;
+};
+
+struct GradParams {
+  const float* fitness;
+  const void* seeds;
+  bool seeds_i32;
+  int64_t pop;
+  int64_t n;        // elements
+  int64_t offset;   // absolute flat index of element 0
+  float scale;      // 1 / (pop * sigma), rounded once from double
+  float* out;
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_forward_f32(const FwdParams& p, hipStream_t stream);
+hipError_t launch_forward_bf16(const FwdParams& p, hipStream_t stream);
+hipError_t launch_gradient(const GradParams& p, hipStream_t stream);
+hipError_t launch_noise(const void* seeds, bool seeds_i32, int64_t pop, int64_t n, int64_t offset,
+                        uint32_t* r_out, float* n_out, hipStream_t stream);
+hipError_t launch_reduce_metric(const float* center, const void* seeds, bool seeds_i32, int64_t pop,
+                                int64_t n, float sigma, int64_t offset, float* out,
+                                hipStream_t stream);
+
+// Largest grid.x the launchers use (they loop inside the kernel beyond it).
+constexpr int64_t kMaxGridX = 0x7FFFFFFF;
+
+}  // namespace vn
