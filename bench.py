@@ -80,6 +80,17 @@ class Step:
         self.gbs = [None if L.bias is None else torch.empty(L.out_features, dtype=torch.float32, device=device)
                     for L in wl.layers]
 
+    def forward_only(self, math):
+        """Forward of every layer in the given math mode (for a side measurement)."""
+        wl, vn = self.wl, self.vn
+        h = self.x
+        n = len(self.layers)
+        for li, (L, w, b) in enumerate(self.layers):
+            act = "relu" if (wl.relu_between and li < n - 1) else None
+            vn.virtual_perturbed_linear(h, w, b, self.seeds, wl.sigma, L.w_offset, activation=act,
+                                        out=self.ys[li], math=math)
+            h = self.ys[li]
+
     def run(self, events=None):
         """events: optional list to which (name, start_event, end_event) are appended."""
         wl, vn, torch = self.wl, self.vn, self.torch
@@ -273,6 +284,18 @@ def main():
             "per_launch_ms": {k: round(v, 4) for k, v in avg_ms.items()},
         },
     }
+    if wl.dtype == "f32":
+        # side measurement: the same forward on the fp32 matrix cores (math mode "f32")
+        for _ in range(2):
+            step.forward_only("f32")
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            step.forward_only("f32")
+        b.record()
+        torch.cuda.synchronize()
+        result["breakdown"]["forward_ms_fp32_matrix_cores"] = round(a.elapsed_time(b) / args.steps, 4)
+        result["config"]["forward_math"] = "fp32 operands as three bf16 matrix-core products, fp32 accumulation"
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
     print(json.dumps(result), flush=True)

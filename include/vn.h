@@ -55,7 +55,7 @@ typedef enum vn_status {
   VN_ERR_NULL = 1,      /* a required pointer is NULL while its extent is > 0            */
   VN_ERR_SHAPE = 2,     /* negative size, or x_pop_stride not in {0, batch*in}           */
   VN_ERR_VALUE = 3,     /* sigma not finite, sigma == 0 in a gradient, pop_size <= 0 in
-                           a gradient, offset < 0, unknown activation                   */
+                           a gradient, offset < 0, unknown activation or math mode      */
   VN_ERR_DTYPE = 4,     /* unknown vn_dtype / vn_index_dtype                             */
   VN_ERR_OVERFLOW = 5,  /* offset + out*in + out, a size product or a prefix sum
                            exceeds INT64_MAX, or a grid dimension limit is exceeded      */
@@ -77,6 +77,15 @@ typedef enum vn_activation {
   VN_ACT_NONE = 0,      /* Y as defined above                                            */
   VN_ACT_RELU = 1       /* max(Y, 0) applied in the same kernel (for chaining layers)    */
 } vn_activation;
+
+typedef enum vn_math {
+  VN_MATH_DEFAULT = 0,  /* bf16 operands: one bf16 matrix-core product per element pair.
+                           fp32 operands: each operand split into bf16 hi + lo, products
+                           hi*hi + hi*lo + lo*hi on the bf16 matrix cores (relative error
+                           about 2^-16 per product), fp32 accumulation                    */
+  VN_MATH_F32 = 1       /* fp32 operands only: fp32 matrix-core products, fp32 accumulation.
+                           Slower on gfx950, where fp32 MFMAs do not overlap the hash    */
+} vn_math;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* vn_status_string(int status);
@@ -116,15 +125,16 @@ int vn_compute_offsets(const int64_t* dims, const int32_t* ndims, int32_t n_bloc
  *   sigma         perturbation scale (finite; 0 gives the plain linear layer)
  *   offset        flat noise offset of this weight block (>= 0)
  *   activation    VN_ACT_NONE or VN_ACT_RELU
+ *   math          vn_math (VN_MATH_F32 requires dtype VN_F32)
  *   y             (pop, batch, out) fp32 output
- * The fp32 variant adds sigma*N to W in fp32 and multiplies on fp32 matrix
- * cores; the bf16 variant forms W + sigma*N in fp32, rounds it to bf16 (nearest
- * even) and multiplies on bf16 matrix cores; both accumulate in fp32.
+ * W + sigma*N is always formed in fp32 (one fma).  The bf16 variant rounds it
+ * to bf16 (nearest even) before the product; the fp32 variant keeps it to
+ * about 16 significant bits (VN_MATH_DEFAULT) or to fp32 (VN_MATH_F32).
  */
 int vn_perturbed_linear(const void* x, int64_t x_pop_stride, const void* w, int32_t dtype,
                         const float* bias, const void* seeds, int32_t seed_dtype,
                         int64_t pop, int64_t batch, int64_t in, int64_t out,
-                        float sigma, int64_t offset, int32_t activation,
+                        float sigma, int64_t offset, int32_t activation, int32_t math,
                         float* y, void* stream);
 
 /*

@@ -80,11 +80,11 @@ def test_compute_offsets_errors(lib):
 
 def fwd(lib, **kw):
     a = dict(x=FAKE, stride=0, w=FAKE, dtype=_lib.VN_F32, b=NULL, seeds=FAKE, sdt=_lib.VN_I64, pop=4,
-             batch=2, i=8, o=3, sigma=0.1, offset=0, act=0, y=FAKE, stream=NULL)
+             batch=2, i=8, o=3, sigma=0.1, offset=0, act=0, math=0, y=FAKE, stream=NULL)
     a.update(kw)
     return lib.vn_perturbed_linear(a["x"], a["stride"], a["w"], a["dtype"], a["b"], a["seeds"], a["sdt"],
                                    a["pop"], a["batch"], a["i"], a["o"], a["sigma"], a["offset"], a["act"],
-                                   a["y"], a["stream"])
+                                   a["math"], a["y"], a["stream"])
 
 
 def test_forward_validation(lib):
@@ -100,6 +100,8 @@ def test_forward_validation(lib):
     assert fwd(lib, sigma=float("inf")) == E.VN_ERR_VALUE
     assert fwd(lib, offset=-1) == E.VN_ERR_VALUE
     assert fwd(lib, act=9) == E.VN_ERR_VALUE
+    assert fwd(lib, math=5) == E.VN_ERR_VALUE
+    assert fwd(lib, math=E.VN_MATH_F32, dtype=E.VN_BF16) == E.VN_ERR_VALUE   # exact fp32 math needs fp32 operands
     assert fwd(lib, offset=2**63 - 20) == E.VN_ERR_OVERFLOW   # offset + out*in + out > INT64_MAX
     assert fwd(lib, o=2**40, i=2**40) == E.VN_ERR_OVERFLOW
     assert fwd(lib, y=NULL) == E.VN_ERR_NULL

@@ -21,6 +21,8 @@ CASES = [
     (4, 64, 256, 256, "f32", True, True, 2**40),    # shared x, huge offset
     (6, 100, 96, 129, "f32", True, False, 5),       # 128-row variant, ragged out
     (3, 200, 64, 65, "f32", False, False, 0),       # 256-row variant
+    (2, 16, 100, 300, "f32", True, False, 8),       # 16-row variant with k tail (100 = 64 + 36)
+    (3, 3, 130, 20, "bf16", True, True, 2),         # 16-row bf16 variant with k tail
     (3, 5, 24, 10, "bf16", True, False, 0),
     (4, 32, 136, 70, "bf16", False, False, 9),
     (2, 64, 1000, 33, "bf16", True, True, 1 << 33),
@@ -29,18 +31,30 @@ CASES = [
 ]
 
 
+CASES_EXACT = [c for c in CASES if c[4] == "f32"]
+
+
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[4]}-p{c[0]}b{c[1]}i{c[2]}o{c[3]}{'-shared' if c[6] else ''}"
                                              for c in CASES])
 def test_ragged_forward(case):
+    _ragged(case, "default")
+
+
+@pytest.mark.parametrize("case", CASES_EXACT, ids=[f"exact-p{c[0]}b{c[1]}i{c[2]}o{c[3]}" for c in CASES_EXACT])
+def test_ragged_forward_exact_f32(case):
+    _ragged(case, "f32")
+
+
+def _ragged(case, math):
     pop, batch, fin, fout, dt, bias, shared, offset = case
-    print(f"ragged forward {case}", flush=True)
+    print(f"ragged forward {case} math={math}", flush=True)
     wl = workloads.make_custom(pop, batch, fin, fout, dtype=dt, bias=bias, shared_x=shared, sigma=0.05,
                                offset=offset, seed=fin + fout, seed_base=-2)
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
     L = wl.layers[0]
     y = vn.virtual_perturbed_linear(to_dev(wl.x, tdt), to_dev(L.weight, tdt),
                                     None if L.bias is None else to_dev(L.bias), to_dev(wl.seeds),
-                                    wl.sigma, offset).cpu().numpy()
+                                    wl.sigma, offset, math=math).cpu().numpy()
     ref = oracle.perturbed_linear(wl.x, L.weight, L.bias, wl.seeds, sigma32(wl.sigma), offset)
     assert_close(y, ref, TOL_BF16 if dt == "bf16" else TOL_F32, str(case))
 

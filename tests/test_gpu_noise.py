@@ -42,21 +42,34 @@ def test_last_indices_of_largest_workloads():
         assert r[0, 0] == oracle.noise_u32_at(s, [idx])[0, 0]
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def split_bf16_cpu(a):
+    """hi = bf16(a), lo = bf16(a - hi), returned as hi + lo (exact in float64)."""
+    hi = bf16_round_cpu(a)
+    lo = bf16_round_cpu(np.asarray(a, dtype=np.float64) - hi)
+    return hi + lo
+
+
+@pytest.mark.parametrize("mode", ["bf16", "f32-default", "f32-exact"])
 @pytest.mark.parametrize("fin,fout", [(16, 37), (40, 33), (100, 70), (256, 130), (13, 9)])
-def test_forward_readout(dtype, fin, fout):
-    """X = I, W = 0, sigma = 1, no bias: Y[i] = N_i^T exactly (bf16: N rounded to bf16)."""
-    print(f"readout {dtype} in={fin} out={fout}", flush=True)
+def test_forward_readout(mode, fin, fout):
+    """X = I, W = 0, sigma = 1, no bias: Y[i] = N_i^T as the operand precision keeps
+    it -- exactly N (fp32 matrix cores), bf16(N) (bf16 operands), or the two-term
+    bf16 split of N (fp32 operands on the bf16 matrix cores)."""
+    print(f"readout {mode} in={fin} out={fout}", flush=True)
     dev = device()
+    dtype = torch.bfloat16 if mode == "bf16" else torch.float32
     pop, offset = 3, 1000
     seeds = np.array([11, -3, 2**40], dtype=np.int64)
     x = torch.eye(fin, dtype=dtype, device=dev)                 # shared (batch=in, in)
     w = torch.zeros((fout, fin), dtype=dtype, device=dev)
-    y = vn.virtual_perturbed_linear(x, w, None, to_dev(seeds), 1.0, offset).cpu().numpy()
+    y = vn.virtual_perturbed_linear(x, w, None, to_dev(seeds), 1.0, offset,
+                                    math="f32" if mode == "f32-exact" else "default").cpu().numpy()
     n = oracle.noise(seeds, fout * fin, offset).reshape(pop, fout, fin)
     want = np.transpose(n, (0, 2, 1))
-    if dtype == torch.bfloat16:
+    if mode == "bf16":
         want = bf16_round_cpu(want)
+    elif mode == "f32-default":
+        want = split_bf16_cpu(want)
     assert np.array_equal(y.astype(np.float64), want)
 
 
@@ -96,7 +109,7 @@ def test_forward_and_gradient_see_the_same_noise():
     seeds = np.array([1, 2, 3, 4], dtype=np.int64)
     s = to_dev(seeds)
     x = torch.eye(fin, device=dev)
-    y = vn.virtual_perturbed_linear(x, torch.zeros((fout, fin), device=dev), None, s, 1.0, offset)
+    y = vn.virtual_perturbed_linear(x, torch.zeros((fout, fin), device=dev), None, s, 1.0, offset, math="f32")
     yb = vn.virtual_perturbed_linear(torch.zeros((1, fin), device=dev), torch.zeros((fout, fin), device=dev),
                                      torch.zeros((fout,), device=dev), s, 1.0, offset)
     for i in range(pop):

@@ -141,6 +141,21 @@ def test_three_layer_gradients():
     assert_close(flat[idx], ref, TOL_F32, "flat gradient of the chained vector")
 
 
+@pytest.mark.parametrize("key", [1, 2, 3])
+def test_single_layer_forward_exact_f32(key):
+    """The fp32 matrix-core math mode on the fp32 workloads."""
+    print(f"workload {key} forward, fp32 matrix cores", flush=True)
+    wl = workloads.make(key)
+    L = wl.layers[0]
+    sig = sigma32(wl.sigma)
+    x, layers, seeds, _ = _dev_inputs(wl)
+    w, b = layers[0]
+    y = vn.virtual_perturbed_linear(x, w, b, seeds, wl.sigma, L.w_offset, math="f32")
+    ids = list(range(wl.pop)) if wl.pop <= 8 else _pick_individuals(wl.pop)
+    ref = oracle.perturbed_linear(wl.x[ids], L.weight, L.bias, wl.seeds[ids], sig, L.w_offset)
+    assert_close(y[ids].cpu().numpy(), ref, TOL_F32, f"workload {key} exact fp32")
+
+
 @pytest.mark.parametrize("key", [2, 5])
 def test_repeat_calls_bit_identical(key):
     print(f"workload {key} determinism", flush=True)

@@ -91,14 +91,17 @@ def compute_offsets(param_shapes: Sequence[Sequence[int]]) -> list:
 def virtual_perturbed_linear(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor],
                              seeds: torch.Tensor, sigma: float, offset: int,
                              activation: Optional[str] = None,
-                             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                             out: Optional[torch.Tensor] = None,
+                             math: str = "default") -> torch.Tensor:
     """``Y[i] = X[i] @ (W + sigma*N_i)^T + (b + sigma*nb_i)`` (page entry
     ``virtual_perturbed_linear``).
 
     x: (batch, in) shared by all individuals, or (pop, batch, in); weight (out, in)
     in the same dtype as x (float32 or bfloat16); bias (out,) or None; seeds
     (pop,) int64/int32.  Returns (pop, batch, out) float32.  ``activation`` may
-    be ``"relu"`` to apply max(., 0) in the same kernel.
+    be ``"relu"`` to apply max(., 0) in the same kernel.  ``math``: ``"default"``
+    (float32 operands as three bf16 matrix-core products, about 2^-16 relative
+    per product) or ``"f32"`` (float32 matrix-core products; float32 only).
     """
     lib = _lib.load()
     _require_device("weight", weight)
@@ -138,6 +141,9 @@ def virtual_perturbed_linear(x: torch.Tensor, weight: torch.Tensor, bias: Option
     act = {None: _lib.VN_ACT_NONE, "none": _lib.VN_ACT_NONE, "relu": _lib.VN_ACT_RELU}.get(activation)
     if act is None:
         raise ValueError(f"unknown activation {activation!r}")
+    mm = {"default": _lib.VN_MATH_DEFAULT, "f32": _lib.VN_MATH_F32}.get(math)
+    if mm is None:
+        raise ValueError(f"unknown math mode {math!r}")
     xc = x.contiguous()
     wc = weight.contiguous()
     if out is None:
@@ -147,7 +153,7 @@ def virtual_perturbed_linear(x: torch.Tensor, weight: torch.Tensor, bias: Option
             raise ValueError("out must be a contiguous float32 (pop, batch, out) tensor")
         y = out
     st = lib.vn_perturbed_linear(_ptr(xc), stride, _ptr(wc), dt, _ptr(b), _ptr(s), kind,
-                                 pop, batch, in_f, out_f, float(sigma), int(offset), act,
+                                 pop, batch, in_f, out_f, float(sigma), int(offset), act, mm,
                                  _ptr(y), _stream(dev))
     _lib.check("vn_perturbed_linear", st)
     return y

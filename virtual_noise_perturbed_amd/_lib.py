@@ -16,6 +16,7 @@ VN_OK, VN_ERR_NULL, VN_ERR_SHAPE, VN_ERR_VALUE, VN_ERR_DTYPE, VN_ERR_OVERFLOW, V
 VN_F32, VN_BF16 = 0, 1
 VN_I64, VN_I32 = 0, 1
 VN_ACT_NONE, VN_ACT_RELU = 0, 1
+VN_MATH_DEFAULT, VN_MATH_F32 = 0, 1
 
 # name -> argument types, in the order of include/vn.h
 SIGNATURES = {
@@ -24,7 +25,7 @@ SIGNATURES = {
     "vn_last_hip_error": [],
     "vn_compute_offsets": [c_void_p, c_void_p, c_int32, c_void_p, c_void_p],
     "vn_perturbed_linear": [c_void_p, c_int64, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
-                            c_int64, c_int64, c_int64, c_int64, c_float, c_int64, c_int32,
+                            c_int64, c_int64, c_int64, c_int64, c_float, c_int64, c_int32, c_int32,
                             c_void_p, c_void_p],
     "vn_weight_gradient": [c_void_p, c_void_p, c_int32, c_int64, c_int64, c_int64, c_float, c_int64,
                            c_void_p, c_void_p],

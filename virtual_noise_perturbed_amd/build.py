@@ -16,6 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvn.so")
+PROBE = os.path.join(PKG, "vn_probe")
 ARCH = "gfx950"
 
 SOURCES = ["vn_kernels.hip", "vn_api.cpp"]
@@ -54,7 +55,22 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     if verbose and errs.strip():
         print(errs, file=sys.stderr)
     os.replace(out_tmp, LIB)
+    build_probe(verbose)
     return LIB
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The instruction-rate / hash-throughput calibration probe (an executable)."""
+    out_tmp = PROBE + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", CSRC, os.path.join(CSRC, "vn_probe.hip"), "-o", out_tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on the probe ({res.returncode}):\n{errs}")
+    os.replace(out_tmp, PROBE)
+    return PROBE
 
 
 if __name__ == "__main__":

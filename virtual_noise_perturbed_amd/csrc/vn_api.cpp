@@ -120,7 +120,8 @@ int vn_compute_offsets(const int64_t* dims, const int32_t* ndims, int32_t n_bloc
 
 int vn_perturbed_linear(const void* x, int64_t x_pop_stride, const void* w, int32_t dtype, const float* bias,
                         const void* seeds, int32_t seed_dtype, int64_t pop, int64_t batch, int64_t in, int64_t out,
-                        float sigma, int64_t offset, int32_t activation, float* y, void* stream) {
+                        float sigma, int64_t offset, int32_t activation, int32_t math, float* y,
+                        void* stream) {
   bool i32 = false;
   if (dtype != VN_F32 && dtype != VN_BF16) return VN_ERR_DTYPE;
   int st = seed_kind(seed_dtype, &i32);
@@ -132,6 +133,8 @@ int vn_perturbed_linear(const void* x, int64_t x_pop_stride, const void* w, int3
   if (!std::isfinite(sigma)) return VN_ERR_VALUE;
   if (offset < 0) return VN_ERR_VALUE;
   if (activation != VN_ACT_NONE && activation != VN_ACT_RELU) return VN_ERR_VALUE;
+  if (math != VN_MATH_DEFAULT && math != VN_MATH_F32) return VN_ERR_VALUE;
+  if (math == VN_MATH_F32 && dtype != VN_F32) return VN_ERR_VALUE;
   // Largest noise index used: offset + out*in + out - 1 (bias); all in int64.
   int64_t oi, last, ysize, xsize;
   if (!mul_ok(out, in, &oi) || !add_ok(oi, out, &last) || !add_ok(offset, last, &last)) return VN_ERR_OVERFLOW;
@@ -162,7 +165,8 @@ int vn_perturbed_linear(const void* x, int64_t x_pop_stride, const void* w, int3
   p.relu = activation == VN_ACT_RELU;
   p.y = y;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(dtype == VN_F32 ? vn::launch_forward_f32(p, s) : vn::launch_forward_bf16(p, s));
+  if (dtype == VN_BF16) return hip_status(vn::launch_forward_bf16(p, s));
+  return hip_status(math == VN_MATH_F32 ? vn::launch_forward_f32_exact(p, s) : vn::launch_forward_f32(p, s));
 }
 
 int vn_flat_gradient(const float* fitness, const void* seeds, int32_t seed_dtype, int64_t pop_size, int64_t n,

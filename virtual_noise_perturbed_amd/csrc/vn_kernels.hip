@@ -32,6 +32,8 @@
 //    tiles of one individual, which share its X rows) land on the same XCD and
 //    its L2, given that the hardware deals workgroups round-robin over 8 XCDs.
 
+#include <type_traits>
+
 #include "vn_device.hpp"
 #include "vn_launch.hpp"
 
@@ -270,6 +272,289 @@ __global__ __launch_bounds__(256, WAVES) void forward_kernel(FwdParams p, int64_
   }
 }
 
+// ---------------------------------------------------------------------------
+// Forward on the bf16 matrix cores with X staged through LDS.
+//
+// On gfx950 the fp32 MFMAs occupy the SIMD like VALU work (they do not run
+// beside the integer hash), while bf16 MFMAs largely do.  This kernel
+// therefore multiplies on v_mfma_f32_{32x32x16,16x16x32}_bf16 with fp32
+// accumulation:
+//   bf16 operands: A = X, B = bf16(W + sigma N) (one product);
+//   fp32 operands (SPLIT): every operand v is split into hi = bf16(v) and
+//     lo = bf16(v - hi) and the product is hi_x*hi_w + hi_x*lo_w + lo_x*hi_w,
+//     which leaves a relative error of about 2^-16 per product (the dropped
+//     lo*lo term and the split residuals); the sum is accumulated in fp32.
+// The X rows of a k-chunk are loaded once per workgroup (not once per wave),
+// split if needed, and kept in a double-buffered LDS tile that all 4 waves
+// read; one barrier per chunk.  The noise side is as in forward_kernel:
+// each lane generates its column's run of R = 16 consecutive k in registers.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> one dword of two bf16 (nearest even), one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = __builtin_convertvector((f32x2){a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+// The two bf16 halves of a packed dword back to fp32 (exact).
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
+
+template <typename IN_T, bool SPLIT, int DIM, int MB, int NB, int WAVES, bool VEC>
+__global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int64_t n_tiles) {
+  using MF = Mfma<__bf16, DIM>;
+  using Acc = typename MF::Acc;
+  constexpr int H = MF::H;            // k-slot groups per MFMA
+  constexpr int R = 16;               // k per lane per chunk
+  constexpr int T = R / 8;            // MFMAs per (row block, column block) per chunk
+  constexpr int KC = H * R;           // k per chunk: 32 (DIM 32) or 64 (DIM 16)
+  constexpr int ROWS = MB * DIM;
+  constexpr int NT = 4 * NB * DIM;
+  constexpr int STRIDE = KC + 8;      // LDS row pitch in bf16 (16-byte pad against bank conflicts)
+  constexpr int PLANES = SPLIT ? 2 : 1;
+  constexpr int PLANE = ROWS * STRIDE;
+  constexpr int BUF = PLANES * PLANE;
+  constexpr int SEG_PER_ROW = KC / 8;                 // a segment is 8 consecutive k of one row
+  constexpr int NSEG = ROWS * SEG_PER_ROW;
+  constexpr int SEG_PER_THREAD = (NSEG + 255) / 256;
+  constexpr uint64_t kChunkStep = gamma_times(KC);
+  static_assert(!SPLIT || sizeof(IN_T) == 4, "split is for fp32 operands");
+
+  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane % DIM;
+  const int lh = lane / DIM;
+
+  const int64_t in = p.in, out = p.out, batch = p.batch;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * ROWS;
+  const int64_t nfull = VEC ? in / KC : 0;            // chunks taken on the unguarded path
+  const int64_t nchunks = (in + KC - 1) / KC;
+
+  const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t i = L / n_tiles;
+  const int64_t tile = L - i * n_tiles;
+  const uint64_t s = load_seed(p.seeds, p.seeds_i32, i);
+  const IN_T* __restrict__ xi = static_cast<const IN_T*>(p.x) + i * p.x_pop_stride;
+  const IN_T* __restrict__ w = static_cast<const IN_T*>(p.w);
+
+  // ---- B side: this lane's columns, their W rows and noise states.  Columns
+  // past `out` read the last column: they only feed discarded outputs.
+  const int64_t jbase = tile * NT + wave * (NB * DIM);
+  const IN_T* wrow[NB];
+  uint64_t z[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    int64_t j = jbase + nb * DIM + ln;
+    j = j < out ? j : out - 1;
+    wrow[nb] = w + j * in + lh * R;
+    z[nb] = state_of(s, static_cast<uint64_t>(p.offset + j * in + lh * R));
+  }
+
+  // ---- A side: this thread's segments of the X tile.  Segment q covers row
+  // q / SEG_PER_ROW and k = (q % SEG_PER_ROW) * 8 .. + 8 of the chunk.  Rows
+  // past `batch` read the last row: they only feed discarded outputs.
+  const IN_T* xsrc[SEG_PER_THREAD];
+  int xdst[SEG_PER_THREAD];
+#pragma unroll
+  for (int u = 0; u < SEG_PER_THREAD; ++u) {
+    const int q = tid + u * 256;
+    const int row = q / SEG_PER_ROW;
+    const int kk = (q % SEG_PER_ROW) * 8;
+    int64_t b = m0 + row;
+    b = b < batch ? b : batch - 1;
+    xsrc[u] = xi + b * in + kk;
+    xdst[u] = (q < NSEG) ? row * STRIDE + kk : -1;
+  }
+  IN_T xs[SEG_PER_THREAD][8];
+  auto load_x = [&](int64_t c, bool guarded) {
+    const int64_t k0 = c * KC;
+#pragma unroll
+    for (int u = 0; u < SEG_PER_THREAD; ++u) {
+      if (NSEG % 256 != 0 && xdst[u] < 0) continue;
+      const IN_T* src = xsrc[u] + k0;
+      if (!guarded) {
+#pragma unroll
+        for (int h = 0; h < static_cast<int>(8 * sizeof(IN_T) / 16); ++h) {
+          const uint4 v = *reinterpret_cast<const uint4*>(src + h * (16 / sizeof(IN_T)));
+          __builtin_memcpy(&xs[u][h * (16 / sizeof(IN_T))], &v, 16);
+        }
+      } else {
+        const int64_t kmax = in - (k0 + (xdst[u] % STRIDE));   // valid k left in this segment
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xs[u][e] = (e < kmax) ? src[e] : static_cast<IN_T>(0.0f);
+      }
+    }
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < SEG_PER_THREAD; ++u) {
+      if (NSEG % 256 != 0 && xdst[u] < 0) continue;
+      uint4 hi, lo;
+      if constexpr (sizeof(IN_T) == 2) {
+        __builtin_memcpy(&hi, &xs[u][0], 16);   // bf16 operands go to LDS as they are
+      } else {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = to_f32(xs[u][2 * e]), b = to_f32(xs[u][2 * e + 1]);
+          hw[e] = pack_bf16x2(a, b);
+          if constexpr (SPLIT) lw[e] = pack_bf16x2(a - bf16_lo_to_f32(hw[e]), b - bf16_hi_to_f32(hw[e]));
+        }
+        __builtin_memcpy(&hi, hw, 16);
+        if constexpr (SPLIT) __builtin_memcpy(&lo, lw, 16);
+      }
+      *reinterpret_cast<uint4*>(&lds[buf * BUF + xdst[u]]) = hi;
+      if constexpr (SPLIT) *reinterpret_cast<uint4*>(&lds[buf * BUF + PLANE + xdst[u]]) = lo;
+    }
+  };
+
+  Acc acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = Acc{};
+
+  // One k-chunk.  GUARDED: the last, partial chunk (or any chunk when the
+  // operands are not 16-byte aligned): element loads, k past `in` zeroed.
+  auto chunk = [&](int64_t c, auto guarded_tag) {
+    constexpr bool GUARDED = decltype(guarded_tag)::value;
+    const int buf = static_cast<int>(c & 1);
+    // W runs of this chunk: the loads fly while the noise is generated.
+    IN_T wv[NB][R];
+    int valid = R;
+    if constexpr (GUARDED) {
+      const int64_t left = in - c * KC;
+      valid = left >= KC ? R : static_cast<int>(left) - lh * R;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) load_run_guarded<IN_T, R>(wv[nb], wrow[nb] + c * KC, valid);
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) load_run<IN_T, R, true>(wv[nb], wrow[nb] + c * KC);
+    }
+    // X of the next chunk, into registers (stored to the other LDS buffer below).
+    const bool has_next = c + 1 < nchunks;
+    if (has_next) load_x(c + 1, c + 1 >= nfull);
+    // Noise for the lane's runs: consecutive k step the state by +GAMMA.
+    float nz[NB][R];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      uint64_t zt = z[nb];
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        nz[nb][t] = noise_of_state(zt);
+        zt += kGamma;
+      }
+      z[nb] += kChunkStep;
+    }
+    // Perturbed weights -> packed bf16 B fragments.
+    uint32_t bhi[NB][R / 2], blo[NB][R / 2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int e = 0; e < R / 2; ++e) {
+        float a = __builtin_fmaf(p.sigma, nz[nb][2 * e], to_f32(wv[nb][2 * e]));
+        float b = __builtin_fmaf(p.sigma, nz[nb][2 * e + 1], to_f32(wv[nb][2 * e + 1]));
+        if constexpr (GUARDED) {
+          a = (2 * e < valid) ? a : 0.0f;
+          b = (2 * e + 1 < valid) ? b : 0.0f;
+        }
+        bhi[nb][e] = pack_bf16x2(a, b);
+        if constexpr (SPLIT) blo[nb][e] = pack_bf16x2(a - bf16_lo_to_f32(bhi[nb][e]), b - bf16_hi_to_f32(bhi[nb][e]));
+      }
+    }
+    // Matrix cores: A fragments from LDS, B fragments from registers.
+    const __bf16* abase = &lds[buf * BUF + ln * STRIDE + lh * R];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(abase + mb * DIM * STRIDE + t * 8);
+        bf16x8 alo;
+        if constexpr (SPLIT) alo = *reinterpret_cast<const bf16x8*>(abase + PLANE + mb * DIM * STRIDE + t * 8);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&bhi[nb][t * 4]));
+          if constexpr (SPLIT) {
+            const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&blo[nb][t * 4]));
+            acc[mb][nb] = mfma_bf16<DIM>(alo, bh, acc[mb][nb]);
+            acc[mb][nb] = mfma_bf16<DIM>(ahi, bl, acc[mb][nb]);
+          }
+          acc[mb][nb] = mfma_bf16<DIM>(ahi, bh, acc[mb][nb]);
+        }
+      }
+    }
+    if (has_next) store_x(buf ^ 1);
+    __syncthreads();
+  };
+
+  if (nchunks > 0) {
+    load_x(0, nfull == 0);
+    store_x(0);
+  }
+  __syncthreads();
+  for (int64_t c = 0; c < nfull; ++c) chunk(c, std::false_type{});
+  for (int64_t c = nfull; c < nchunks; ++c) chunk(c, std::true_type{});
+
+  // Epilogue: bias b_j + sigma nb_i[j] with nb at offset + out*in + j.
+  const int rb = MF::row_base(lane);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int64_t j = jbase + nb * DIM + ln;
+    if (j >= out) continue;
+    float bj = 0.0f;
+    if (p.bias != nullptr) {
+      const float nz = noise_of_state(state_of(s, static_cast<uint64_t>(p.offset + out * in + j)));
+      bj = __builtin_fmaf(p.sigma, nz, p.bias[j]);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int64_t row0 = m0 + mb * DIM + rb;
+      float* __restrict__ yp = p.y + (i * batch + row0) * out + j;
+#pragma unroll
+      for (int v = 0; v < MF::NACC; ++v) {
+        const int ro = MF::row_off(v);
+        if (row0 + ro < batch) {
+          float val = acc[mb][nb][v] + bj;
+          if (p.relu) val = val > 0.0f ? val : 0.0f;
+          yp[static_cast<int64_t>(ro) * out] = val;
+        }
+      }
+    }
+  }
+}
+
+template <typename IN_T, bool SPLIT, int DIM, int MB, int NB, int WAVES>
+static hipError_t launch_mm_cfg(const FwdParams& p, hipStream_t stream) {
+  constexpr int NT = 4 * NB * DIM;
+  constexpr int ROWS = MB * DIM;
+  const int64_t n_tiles = (p.out + NT - 1) / NT;
+  const int64_t total = p.pop * n_tiles;
+  const int64_t m_tiles = (p.batch + ROWS - 1) / ROWS;
+  if (total > kMaxGridX || m_tiles > 65535) return hipErrorInvalidConfiguration;
+  dim3 grid(static_cast<unsigned>(total), static_cast<unsigned>(m_tiles));
+  // 16-byte loads need 16-byte aligned bases, rows and individual strides.
+  const int64_t per = 16 / static_cast<int64_t>(sizeof(IN_T));
+  const bool vec = (reinterpret_cast<uintptr_t>(p.x) % 16 == 0) && (reinterpret_cast<uintptr_t>(p.w) % 16 == 0) &&
+                   (p.in % per == 0) && (p.x_pop_stride % per == 0);
+  if (vec)
+    forward_mm_kernel<IN_T, SPLIT, DIM, MB, NB, WAVES, true><<<grid, 256, 0, stream>>>(p, n_tiles);
+  else
+    forward_mm_kernel<IN_T, SPLIT, DIM, MB, NB, WAVES, false><<<grid, 256, 0, stream>>>(p, n_tiles);
+  return hipGetLastError();
+}
+
+template <typename IN_T, bool SPLIT>
+static hipError_t launch_mm_dtype(const FwdParams& p, hipStream_t stream) {
+  if (p.batch <= 16) return launch_mm_cfg<IN_T, SPLIT, 16, 1, 2, 2>(p, stream);
+  if (p.batch <= 32) return launch_mm_cfg<IN_T, SPLIT, 32, 1, 2, 2>(p, stream);
+  if (p.batch <= 64) return launch_mm_cfg<IN_T, SPLIT, 32, 2, 2, 2>(p, stream);
+  if (p.batch <= 128) return launch_mm_cfg<IN_T, SPLIT, 32, 4, 1, 2>(p, stream);
+  return launch_mm_cfg<IN_T, SPLIT, 32, 8, 1, 2>(p, stream);
+}
+
 // WAVES: waves per SIMD the register allocation must allow.
 template <typename DT, int DIM, int MB, int NB, int T, int WAVES>
 static hipError_t launch_fwd_cfg(const FwdParams& p, hipStream_t stream) {
@@ -307,10 +592,13 @@ static hipError_t launch_fwd_dtype(const FwdParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_forward_f32(const FwdParams& p, hipStream_t stream) {
+  return launch_mm_dtype<float, true>(p, stream);
+}
+hipError_t launch_forward_f32_exact(const FwdParams& p, hipStream_t stream) {
   return launch_fwd_dtype<float, 4, 8, 4>(p, stream);
 }
 hipError_t launch_forward_bf16(const FwdParams& p, hipStream_t stream) {
-  return launch_fwd_dtype<__bf16, 2, 2, 1>(p, stream);
+  return launch_mm_dtype<__bf16, false>(p, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -33,7 +33,8 @@ struct GradParams {
 };
 
 // Each returns hipSuccess or the launch error.
-hipError_t launch_forward_f32(const FwdParams& p, hipStream_t stream);
+hipError_t launch_forward_f32(const FwdParams& p, hipStream_t stream);        // split-bf16 matrix cores
+hipError_t launch_forward_f32_exact(const FwdParams& p, hipStream_t stream);  // fp32 matrix cores
 hipError_t launch_forward_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_gradient(const GradParams& p, hipStream_t stream);
 hipError_t launch_noise(const void* seeds, bool seeds_i32, int64_t pop, int64_t n, int64_t offset,

@@ -1,0 +1,165 @@
+// Calibration probe for the ALU roofline of the noise hash on gfx950.
+//
+// Measures (1) the issue rate of every vector instruction the hash sequence
+// uses, as lane-operations per second and as a fraction of the full 32-bit
+// rate (64 lane-ops per CU per clock), and (2) the throughput of the hash
+// sequence of vn_device.hpp itself, in hashes per second.
+//
+// Each probe kernel runs 16 independent dependency chains per lane (so
+// latency never limits issue) at 8 waves per SIMD; the only memory access
+// is one store per thread of a checksum, into a buffer sized to the grid.
+// Prints one JSON object per line.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "vn_device.hpp"
+
+#define CHECK(x)                                                                       \
+  do {                                                                                 \
+    hipError_t e_ = (x);                                                               \
+    if (e_ != hipSuccess) {                                                            \
+      std::fprintf(stderr, "HIP error %s at %s:%d\n", hipGetErrorString(e_), __FILE__, __LINE__); \
+      std::exit(1);                                                                    \
+    }                                                                                  \
+  } while (0)
+
+constexpr int kThreads = 256;
+constexpr int kChains = 16;
+
+// 32-bit ops: a = op(a, b) on 16 chains.
+#define PROBE32(NAME, ASM)                                                              \
+  __global__ __launch_bounds__(kThreads) void NAME(uint32_t* out, int iters, uint32_t seed) { \
+    uint32_t a[kChains];                                                                \
+    const uint32_t b = seed * 2654435761u + threadIdx.x;                                \
+    _Pragma("unroll") for (int c = 0; c < kChains; ++c) a[c] = threadIdx.x + c * 977u + seed; \
+    for (int it = 0; it < iters; ++it) {                                                \
+      _Pragma("unroll") for (int c = 0; c < kChains; ++c) asm volatile(ASM : "+v"(a[c]) : "v"(b)); \
+    }                                                                                   \
+    uint32_t r = 0;                                                                     \
+    _Pragma("unroll") for (int c = 0; c < kChains; ++c) r ^= a[c];                      \
+    out[blockIdx.x * kThreads + threadIdx.x] = r;                                       \
+  }
+
+// 64-bit ops on 16 chains of register pairs (%1: 64-bit operand, %2, %3: 32-bit operands).
+#define PROBE64(NAME, ASM)                                                              \
+  __global__ __launch_bounds__(kThreads) void NAME(uint32_t* out, int iters, uint32_t seed) { \
+    uint64_t a[kChains];                                                                \
+    const uint64_t b = (static_cast<uint64_t>(seed) << 32) | threadIdx.x;               \
+    const uint32_t b1 = seed * 2654435761u + threadIdx.x, b2 = seed ^ 0x9E3779B9u;      \
+    _Pragma("unroll") for (int c = 0; c < kChains; ++c) a[c] = threadIdx.x + c * 977ull + seed; \
+    for (int it = 0; it < iters; ++it) {                                                \
+      _Pragma("unroll") for (int c = 0; c < kChains; ++c)                               \
+        asm volatile(ASM : "+v"(a[c]) : "v"(b), "v"(b1), "v"(b2) : "vcc");             \
+    }                                                                                   \
+    uint64_t r = 0;                                                                     \
+    _Pragma("unroll") for (int c = 0; c < kChains; ++c) r ^= a[c];                      \
+    out[blockIdx.x * kThreads + threadIdx.x] = static_cast<uint32_t>(r ^ (r >> 32));    \
+  }
+
+PROBE32(p_xor, "v_xor_b32 %0, %0, %1")
+PROBE32(p_add_u32, "v_add_u32 %0, %0, %1")
+PROBE32(p_mul_lo, "v_mul_lo_u32 %0, %0, %1")
+PROBE32(p_mul_hi, "v_mul_hi_u32 %0, %0, %1")
+PROBE32(p_mul_u24, "v_mul_u32_u24 %0, %0, %1")
+PROBE32(p_alignbit, "v_alignbit_b32 %0, %0, %1, 30")
+PROBE32(p_add3, "v_add3_u32 %0, %0, %1, %0")
+PROBE32(p_lshr, "v_lshrrev_b32 %0, 8, %0")
+PROBE32(p_cvt, "v_cvt_f32_u32 %0, %0")
+PROBE32(p_fma, "v_fma_f32 %0, %0, %1, %0")
+PROBE64(p_mad64, "v_mad_u64_u32 %0, vcc, %2, %3, %0")
+PROBE64(p_shr64, "v_lshrrev_b64 %0, 30, %0")
+PROBE64(p_add64, "v_lshl_add_u64 %0, %0, 0, %1")
+
+// The shipped hash: Weyl-stepped states, low 32 bits of the finalizer.
+__global__ __launch_bounds__(kThreads) void p_hash(uint32_t* out, int iters, uint32_t seed) {
+  constexpr int S = 8;
+  uint64_t z[S];
+  const uint64_t g = blockIdx.x * kThreads + threadIdx.x;
+#pragma unroll
+  for (int c = 0; c < S; ++c) z[c] = vn::state_of(seed, g * 64 + c);
+  uint32_t acc = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < S; ++c) {
+      acc ^= vn::mix_lo32(z[c]);
+      z[c] += vn::gamma_times(S);
+    }
+  }
+  out[g] = acc;
+}
+
+struct Probe {
+  const char* name;
+  void (*fn)(uint32_t*, int, uint32_t);
+  int per_iter;   // instructions (or hashes) per lane per iteration
+  const char* what;
+};
+
+int main(int argc, char** argv) {
+  int dev = 0;
+  CHECK(hipSetDevice(dev));
+  hipDeviceProp_t prop;
+  CHECK(hipGetDeviceProperties(&prop, dev));
+  int clock_khz = 0;
+  CHECK(hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeClockRate, dev));
+  const int cus = prop.multiProcessorCount;
+  const int blocks = cus * 8;  // 8 blocks of 4 waves per CU = 8 waves per SIMD
+  const int iters = argc > 1 ? std::atoi(argv[1]) : 2048;
+  std::printf("{\"device\": \"%s\", \"gcn_arch\": \"%s\", \"cus\": %d, \"clock_mhz\": %.0f, \"blocks\": %d, "
+              "\"threads\": %d, \"iters\": %d}\n",
+              prop.name, prop.gcnArchName, cus, clock_khz / 1e3, blocks, kThreads, iters);
+  uint32_t* out = nullptr;
+  CHECK(hipMalloc(&out, sizeof(uint32_t) * blocks * kThreads));
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  const Probe probes[] = {
+      {"v_xor_b32", p_xor, kChains, "32-bit"},
+      {"v_add_u32", p_add_u32, kChains, "32-bit"},
+      {"v_mul_lo_u32", p_mul_lo, kChains, "32-bit"},
+      {"v_mul_hi_u32", p_mul_hi, kChains, "32-bit"},
+      {"v_mul_u32_u24", p_mul_u24, kChains, "32-bit"},
+      {"v_alignbit_b32", p_alignbit, kChains, "32-bit"},
+      {"v_add3_u32", p_add3, kChains, "32-bit"},
+      {"v_lshrrev_b32", p_lshr, kChains, "32-bit"},
+      {"v_cvt_f32_u32", p_cvt, kChains, "32-bit"},
+      {"v_fma_f32", p_fma, kChains, "32-bit"},
+      {"v_mad_u64_u32", p_mad64, kChains, "64-bit"},
+      {"v_lshrrev_b64", p_shr64, kChains, "64-bit"},
+      {"v_lshl_add_u64", p_add64, kChains, "64-bit"},
+      {"hash", p_hash, 8, "hash"},
+  };
+  const double peak_lane_ops = static_cast<double>(cus) * 64.0 * clock_khz * 1e3;
+  for (const Probe& pr : probes) {
+    // warm-up, then the best of 3 timed launches
+    pr.fn<<<blocks, kThreads>>>(out, iters / 8, 1u);
+    CHECK(hipGetLastError());
+    CHECK(hipDeviceSynchronize());
+    float best = 1e30f;
+    for (int rep = 0; rep < 3; ++rep) {
+      CHECK(hipEventRecord(e0));
+      pr.fn<<<blocks, kThreads>>>(out, iters, 2u + rep);
+      CHECK(hipEventRecord(e1));
+      CHECK(hipEventSynchronize(e1));
+      float ms = 0;
+      CHECK(hipEventElapsedTime(&ms, e0, e1));
+      if (ms < best) best = ms;
+    }
+    const double ops = static_cast<double>(blocks) * kThreads * iters * pr.per_iter;
+    const double rate = ops / (best * 1e-3);
+    if (std::strcmp(pr.what, "hash") == 0) {
+      std::printf("{\"probe\": \"hash\", \"ms\": %.4f, \"hashes_per_s\": %.4e, \"lane_cycles_per_hash\": %.2f}\n", best,
+                  rate, peak_lane_ops / rate);
+    } else {
+      std::printf("{\"probe\": \"%s\", \"ms\": %.4f, \"lane_ops_per_s\": %.4e, \"rate_vs_full\": %.3f}\n", pr.name,
+                  best, rate, rate / peak_lane_ops);
+    }
+    std::fflush(stdout);
+  }
+  CHECK(hipFree(out));
+  return 0;
+}
