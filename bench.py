@@ -29,19 +29,62 @@ if ROOT not in sys.path:
 
 METRIC = "perturbed-linear TFLOP/s + noise-gradient elements/s, % of roofline, 1 GPU"
 
-# MI355X (gfx950) unit counts and clock used for the ALU roofline.
-N_CU = 256
-LANES_PER_CU_CLK = 64          # 4 SIMDs x 16 lanes: full-rate 32-bit VALU lane-ops per clock per CU
+# ---------------------------------------------------------------------------
+# ALU roofline of the noise hash on MI355X (gfx950).
+#
+# 256 CUs x 4 SIMDs at 2.4 GHz.  A wave64 VALU instruction occupies a SIMD for
+# 4 / rate cycles, where `rate` is the instruction's issue rate relative to 64
+# lane-ops per CU per clock, measured by virtual_noise_perturbed_amd/vn_probe
+# (summary in profiles/vn_probe_gfx950.txt).  The hash sequence shipped in
+# every kernel (from the gfx950 assembly of vn_device.hpp) is, per noise
+# element: 1 v_lshl_add_u64 (state step), 2 x [v_lshrrev_b64, 2 v_xor_b32,
+# 2 v_mul_lo_u32, v_mad_u64_u32, v_add3_u32] (xor-shift and 64-bit multiply
+# by GAMMA), v_alignbit_b32 + v_xor_b32 (final xor-shift, low word),
+# v_lshrrev_b32 (r >> 8) and v_cvt_f32_u32.  Its issue cost bounds how many
+# noise elements per second the chip can produce; both kernels need at least
+# this work per element, so it is the peak their rates are compared with.
+N_SIMD = 256 * 4
 CLOCK_HZ = 2.4e9
-# Lane-cycles per noise element of the shipped kernels (ISA count of one hash,
-# quarter-rate 32-bit multiplies counted 4): state add 1, 2 x (64-bit shift 1,
-# xor 2, multiply 3 x 4 + add 1), final shift+xor 2, >>8 1, cvt 1, fma 1.
-HASH_LANE_CYCLES = {"forward": 39.0, "gradient": 39.0}
+PROBE_RATE = {            # measured issue rate, fraction of 64 lane-ops/CU/clk
+    "v_lshl_add_u64": 0.825, "v_lshrrev_b64": 0.854, "v_xor_b32": 1.314,
+    "v_mul_lo_u32": 0.778, "v_mad_u64_u32": 0.791, "v_add3_u32": 0.885,
+    "v_alignbit_b32": 0.893, "v_lshrrev_b32": 1.485, "v_cvt_f32_u32": 0.849,
+}
+HASH_ISA = {              # instructions per noise element
+    "v_lshl_add_u64": 1, "v_lshrrev_b64": 2, "v_xor_b32": 5, "v_mul_lo_u32": 4,
+    "v_mad_u64_u32": 2, "v_add3_u32": 2, "v_alignbit_b32": 1, "v_lshrrev_b32": 1,
+    "v_cvt_f32_u32": 1,
+}
+HASH_SIMD_CYCLES = sum(n * 4.0 / PROBE_RATE[k] for k, n in HASH_ISA.items())   # per wave64 element
+HASH_PEAK_PER_S = N_SIMD * 64 * CLOCK_HZ / HASH_SIMD_CYCLES
 HBM_PEAK_GBS = 8000.0
 
+KERNEL_SRC = os.path.join(ROOT, "virtual_noise_perturbed_amd", "csrc", "vn_kernels.hip")
+DEVICE_SRC = os.path.join(ROOT, "virtual_noise_perturbed_amd", "csrc", "vn_device.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
-def hash_peak_per_s(kind: str) -> float:
-    return N_CU * LANES_PER_CU_CLK * CLOCK_HZ / HASH_LANE_CYCLES[kind]
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in (KERNEL_SRC, DEVICE_SRC):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload_key: int, kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none for this kernel or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    ent = rec.get("entries", {}).get(f"{workload_key}:{kernel}")
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
 def parse():
@@ -53,6 +96,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds for the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (to scale memory counters)")
+    ap.add_argument("--only", choices=["forward", "gradient"], default=None,
+                    help="run only one kernel family in the timed steps (for profiling runs)")
     return ap.parse_args()
 
 
@@ -91,6 +138,15 @@ class Step:
                                         out=self.ys[li], math=math)
             h = self.ys[li]
 
+    def gradients_only(self):
+        wl, vn = self.wl, self.vn
+        for li, (L, w, b) in enumerate(self.layers):
+            vn.virtual_flat_gradient(self.fit, self.seeds, L.out_features * L.in_features, wl.sigma, wl.pop,
+                                     L.w_offset, out=self.gws[li])
+            if b is not None:
+                vn.virtual_flat_gradient(self.fit, self.seeds, L.out_features, wl.sigma, wl.pop, L.b_offset,
+                                         out=self.gbs[li])
+
     def run(self, events=None):
         """events: optional list to which (name, start_event, end_event) are appended."""
         wl, vn, torch = self.wl, self.vn, self.torch
@@ -120,6 +176,19 @@ class Step:
             if b is not None:
                 timed(f"grad_b{li}", lambda L=L, g=self.gbs[li]: vn.virtual_flat_gradient(
                     self.fit, self.seeds, L.out_features, wl.sigma, wl.pop, L.b_offset, out=g))
+
+
+def copy_calibration(torch, device):
+    """A plain device-to-device copy of a known number of bytes, under the same
+    counters as the kernels, to scale FETCH_SIZE / WRITE_SIZE."""
+    n = 256 * 1024 * 1024 // 4            # 256 MiB of fp32
+    a = torch.ones(n, dtype=torch.float32, device=device)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                      "launches": 3}))
 
 
 def flops_of(wl) -> float:
@@ -201,8 +270,21 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
     device = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(torch, device)
+        return
     wl = workloads.make(args.workload)
     step = Step(wl, torch, vn, device)
+    if args.only is not None:
+        # profiling aid: the timed steps of one kernel family only
+        for _ in range(args.warmup + args.steps):
+            if args.only == "forward":
+                step.forward_only("default")
+            else:
+                step.gradients_only()
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "workload": wl.name, "launches": args.warmup + args.steps}))
+        return
 
     for _ in range(args.warmup):
         step.run()
@@ -230,25 +312,24 @@ def main():
     L = wl.layers[li]
     if dom.startswith("forward"):
         units = wl.pop * (L.out_features * L.in_features + (L.out_features if L.bias is not None else 0))
-        kind = "forward"
     elif dom.startswith("grad_w"):
         units = wl.pop * L.out_features * L.in_features
-        kind = "gradient"
     else:
         units = wl.pop * L.out_features
-        kind = "gradient"
-    achieved = units / (avg_ms[dom] * 1e-3) / 1e9
-    peak = hash_peak_per_s(kind) / 1e9
+    achieved = units / (avg_ms[dom] * 1e-3)
+    traffic = recorded_traffic(args.workload, dom)
     roofline = {
         "bound": "alu",
         "kernel": dom,
-        "achieved": round(achieved, 2),
-        "peak": round(peak, 2),
-        "unit": "Ghash/s",
-        "frac": round(achieved / peak, 4),
-        "traffic": None,
+        "achieved": round(achieved / 1e9, 2),
+        "peak": round(HASH_PEAK_PER_S / 1e9, 2),
+        "unit": "G noise elements/s",
+        "frac": round(achieved / HASH_PEAK_PER_S, 4),
+        "traffic": traffic,
         "units_per_launch": units,
         "avg_launch_ms": round(avg_ms[dom], 4),
+        "peak_basis": (f"hash issue bound: {HASH_SIMD_CYCLES:.1f} SIMD-cycles per wave64 element "
+                       f"(ISA count x measured issue costs), {N_SIMD} SIMDs x 64 lanes x 2.4 GHz"),
     }
 
     value = flops_of(wl) / (ms_per_step * 1e-3) / 1e12
@@ -273,14 +354,18 @@ def main():
             "sigma": wl.sigma,
             "step": "forward of every layer + weight and bias gradient of every block",
         },
+        "roofline": roofline,
         "breakdown": {
             "forward_ms": round(fwd_ms, 4),
             "gradient_ms": round(grad_ms, 4),
             "forward_tflops": round(flops_of(wl) / (fwd_ms * 1e-3) / 1e12, 3),
             "forward_noise_elements_per_s": fwd_hashes(wl) / (fwd_ms * 1e-3),
             "gradient_elements_per_s": grad_elems(wl) / (grad_ms * 1e-3),
-            "gradient_frac_of_hash_peak": round(grad_elems(wl) / (grad_ms * 1e-3) / hash_peak_per_s("gradient"), 4),
-            "forward_frac_of_hash_peak": round(fwd_hashes(wl) / (fwd_ms * 1e-3) / hash_peak_per_s("forward"), 4),
+            "gradient_frac_of_hash_peak": round(grad_elems(wl) / (grad_ms * 1e-3) / HASH_PEAK_PER_S, 4),
+            "forward_frac_of_hash_peak": round(fwd_hashes(wl) / (fwd_ms * 1e-3) / HASH_PEAK_PER_S, 4),
+            # matrix-core work actually issued (fp32 operands: three bf16 products) vs 2.5 PFLOP/s bf16 dense
+            "forward_mfma_utilization": round(flops_of(wl) * (1 if wl.dtype == "bf16" else 3) /
+                                              (fwd_ms * 1e-3) / 2.5e15, 4),
             "per_launch_ms": {k: round(v, 4) for k, v in avg_ms.items()},
         },
     }

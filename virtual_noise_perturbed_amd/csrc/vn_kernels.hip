@@ -300,14 +300,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
 
-template <typename IN_T, bool SPLIT, int DIM, int MB, int NB, int WAVES, bool VEC>
+template <typename IN_T, bool SPLIT, int DIM, int MB, int NB, int R, int WAVES, bool VEC>
 __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int64_t n_tiles) {
   using MF = Mfma<__bf16, DIM>;
   using Acc = typename MF::Acc;
   constexpr int H = MF::H;            // k-slot groups per MFMA
-  constexpr int R = 16;               // k per lane per chunk
+  static_assert(R % 8 == 0, "R: k per lane per chunk, whole MFMA k-slots");
   constexpr int T = R / 8;            // MFMAs per (row block, column block) per chunk
-  constexpr int KC = H * R;           // k per chunk: 32 (DIM 32) or 64 (DIM 16)
+  constexpr int KC = H * R;           // k per chunk
   constexpr int ROWS = MB * DIM;
   constexpr int NT = 4 * NB * DIM;
   constexpr int STRIDE = KC + 8;      // LDS row pitch in bf16 (16-byte pad against bank conflicts)
@@ -319,6 +319,9 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
   constexpr int SEG_PER_THREAD = (NSEG + 255) / 256;
   constexpr uint64_t kChunkStep = gamma_times(KC);
   static_assert(!SPLIT || sizeof(IN_T) == 4, "split is for fp32 operands");
+  constexpr int kMfmaPerChunk = T * MB * NB * (SPLIT ? 3 : 1);
+  // about 23 VALU instructions per noise element (+3 for the split)
+  constexpr int kValuPerMfma = (NB * R * (SPLIT ? 26 : 23)) / kMfmaPerChunk;
 
   __shared__ __attribute__((aligned(16))) __bf16 lds[2 * BUF];
 
@@ -360,20 +363,22 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
   int xdst[SEG_PER_THREAD];
 #pragma unroll
   for (int u = 0; u < SEG_PER_THREAD; ++u) {
-    const int q = tid + u * 256;
+    // Threads past the last segment (when the tile has fewer than 256 per
+    // pass) repeat one: same source, same LDS slot, same bytes -- this keeps
+    // the pipelined loop free of branches.
+    const int q = (tid + u * 256) % NSEG;
     const int row = q / SEG_PER_ROW;
     const int kk = (q % SEG_PER_ROW) * 8;
     int64_t b = m0 + row;
     b = b < batch ? b : batch - 1;
     xsrc[u] = xi + b * in + kk;
-    xdst[u] = (q < NSEG) ? row * STRIDE + kk : -1;
+    xdst[u] = row * STRIDE + kk;
   }
   IN_T xs[SEG_PER_THREAD][8];
   auto load_x = [&](int64_t c, bool guarded) {
     const int64_t k0 = c * KC;
 #pragma unroll
     for (int u = 0; u < SEG_PER_THREAD; ++u) {
-      if (NSEG % 256 != 0 && xdst[u] < 0) continue;
       const IN_T* src = xsrc[u] + k0;
       if (!guarded) {
 #pragma unroll
@@ -383,6 +388,7 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
         }
       } else {
         const int64_t kmax = in - (k0 + (xdst[u] % STRIDE));   // valid k left in this segment
+        // (xdst % STRIDE is the segment's k offset within the chunk)
 #pragma unroll
         for (int e = 0; e < 8; ++e) xs[u][e] = (e < kmax) ? src[e] : static_cast<IN_T>(0.0f);
       }
@@ -391,7 +397,6 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
   auto store_x = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < SEG_PER_THREAD; ++u) {
-      if (NSEG % 256 != 0 && xdst[u] < 0) continue;
       uint4 hi, lo;
       if constexpr (sizeof(IN_T) == 2) {
         __builtin_memcpy(&hi, &xs[u][0], 16);   // bf16 operands go to LDS as they are
@@ -417,28 +422,28 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = Acc{};
 
-  // One k-chunk.  GUARDED: the last, partial chunk (or any chunk when the
-  // operands are not 16-byte aligned): element loads, k past `in` zeroed.
-  auto chunk = [&](int64_t c, auto guarded_tag) {
-    constexpr bool GUARDED = decltype(guarded_tag)::value;
-    const int buf = static_cast<int>(c & 1);
-    // W runs of this chunk: the loads fly while the noise is generated.
-    IN_T wv[NB][R];
-    int valid = R;
-    if constexpr (GUARDED) {
-      const int64_t left = in - c * KC;
-      valid = left >= KC ? R : static_cast<int>(left) - lh * R;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) load_run_guarded<IN_T, R>(wv[nb], wrow[nb] + c * KC, valid);
-    } else {
+  // Software pipeline over k-chunks: iteration c generates the noise and the
+  // packed B fragments of chunk c+1 on the VALU while the matrix cores work on
+  // chunk c, whose B fragments were made in the previous iteration and whose X
+  // tile sits in LDS buffer c & 1.  The X rows of chunk c+1 reach the other
+  // buffer at the start of iteration c, those of chunk c+2 are loaded into
+  // registers meanwhile; one barrier per iteration.
+  IN_T wv[NB][R];                           // W runs of the chunk being prepared
+  uint32_t bh[NB][R / 2], bl[NB][R / 2];    // packed B fragments of the chunk being multiplied
+
+  auto load_w = [&](int64_t c, bool guarded) {
+    if (!guarded) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) load_run<IN_T, R, true>(wv[nb], wrow[nb] + c * KC);
+    } else {
+      const int64_t left = in - c * KC;
+      const int valid = left >= KC ? R : static_cast<int>(left) - lh * R;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) load_run_guarded<IN_T, R>(wv[nb], wrow[nb] + c * KC, valid);
     }
-    // X of the next chunk, into registers (stored to the other LDS buffer below).
-    const bool has_next = c + 1 < nchunks;
-    if (has_next) load_x(c + 1, c + 1 >= nfull);
-    // Noise for the lane's runs: consecutive k step the state by +GAMMA.
-    float nz[NB][R];
+  };
+  // Noise of chunk c (the lane's runs; consecutive k step the state by +GAMMA).
+  auto make_noise = [&](float (&nz)[NB][R]) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       uint64_t zt = z[nb];
@@ -449,23 +454,31 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
       }
       z[nb] += kChunkStep;
     }
-    // Perturbed weights -> packed bf16 B fragments.
-    uint32_t bhi[NB][R / 2], blo[NB][R / 2];
+  };
+  // W + sigma N of chunk c -> packed bf16 B fragments (hi, and lo when split).
+  auto make_b = [&](const float (&nz)[NB][R], int64_t c, bool guarded) {
+    int valid = R;
+    if (guarded) {
+      const int64_t left = in - c * KC;
+      valid = left >= KC ? R : static_cast<int>(left) - lh * R;
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
       for (int e = 0; e < R / 2; ++e) {
         float a = __builtin_fmaf(p.sigma, nz[nb][2 * e], to_f32(wv[nb][2 * e]));
         float b = __builtin_fmaf(p.sigma, nz[nb][2 * e + 1], to_f32(wv[nb][2 * e + 1]));
-        if constexpr (GUARDED) {
+        if (guarded) {
           a = (2 * e < valid) ? a : 0.0f;
           b = (2 * e + 1 < valid) ? b : 0.0f;
         }
-        bhi[nb][e] = pack_bf16x2(a, b);
-        if constexpr (SPLIT) blo[nb][e] = pack_bf16x2(a - bf16_lo_to_f32(bhi[nb][e]), b - bf16_hi_to_f32(bhi[nb][e]));
+        bh[nb][e] = pack_bf16x2(a, b);
+        if constexpr (SPLIT) bl[nb][e] = pack_bf16x2(a - bf16_lo_to_f32(bh[nb][e]), b - bf16_hi_to_f32(bh[nb][e]));
       }
     }
-    // Matrix cores: A fragments from LDS, B fragments from registers.
+  };
+  // Matrix cores on chunk c: A fragments from LDS buffer `buf`, B from bh/bl.
+  auto multiply = [&](int buf) {
     const __bf16* abase = &lds[buf * BUF + ln * STRIDE + lh * R];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -476,27 +489,61 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
         if constexpr (SPLIT) alo = *reinterpret_cast<const bf16x8*>(abase + PLANE + mb * DIM * STRIDE + t * 8);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&bhi[nb][t * 4]));
+          const bf16x8 bfh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&bh[nb][t * 4]));
           if constexpr (SPLIT) {
-            const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&blo[nb][t * 4]));
-            acc[mb][nb] = mfma_bf16<DIM>(alo, bh, acc[mb][nb]);
-            acc[mb][nb] = mfma_bf16<DIM>(ahi, bl, acc[mb][nb]);
+            const bf16x8 bfl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&bl[nb][t * 4]));
+            acc[mb][nb] = mfma_bf16<DIM>(alo, bfh, acc[mb][nb]);
+            acc[mb][nb] = mfma_bf16<DIM>(ahi, bfl, acc[mb][nb]);
           }
-          acc[mb][nb] = mfma_bf16<DIM>(ahi, bh, acc[mb][nb]);
+          acc[mb][nb] = mfma_bf16<DIM>(ahi, bfh, acc[mb][nb]);
         }
       }
     }
-    if (has_next) store_x(buf ^ 1);
-    __syncthreads();
   };
 
   if (nchunks > 0) {
     load_x(0, nfull == 0);
     store_x(0);
+    load_w(0, nfull == 0);
+    if (nchunks > 1) load_x(1, nfull <= 1);
+    float nz[NB][R];
+    make_noise(nz);
+    make_b(nz, 0, nfull == 0);
   }
   __syncthreads();
-  for (int64_t c = 0; c < nfull; ++c) chunk(c, std::false_type{});
-  for (int64_t c = nfull; c < nchunks; ++c) chunk(c, std::true_type{});
+  // Steady state: chunks c+1 and c+2 are whole, nothing is guarded.
+  int64_t c = 0;
+  for (; c + 2 < nfull; ++c) {
+    store_x(static_cast<int>((c + 1) & 1));
+    load_w(c + 1, false);
+    load_x(c + 2, false);
+    float nz[NB][R];
+    make_noise(nz);
+    multiply(static_cast<int>(c & 1));
+    make_b(nz, c + 1, false);
+    // Interleave: one MFMA, then a share of the noise VALU work, repeatedly,
+    // so the matrix cores run under the hash instead of after it.
+#pragma unroll
+    for (int k = 0; k < kMfmaPerChunk; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+    }
+    __syncthreads();
+  }
+  // The last chunks: same steps with guards.
+  for (; c < nchunks; ++c) {
+    const bool next = c + 1 < nchunks;
+    if (next) {
+      store_x(static_cast<int>((c + 1) & 1));
+      load_w(c + 1, c + 1 >= nfull);
+      if (c + 2 < nchunks) load_x(c + 2, c + 2 >= nfull);
+    }
+    float nz[NB][R];
+    if (next) make_noise(nz);
+    multiply(static_cast<int>(c & 1));
+    if (next) make_b(nz, c + 1, c + 1 >= nfull);
+    __syncthreads();
+  }
 
   // Epilogue: bias b_j + sigma nb_i[j] with nb at offset + out*in + j.
   const int rb = MF::row_base(lane);
@@ -526,7 +573,7 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
   }
 }
 
-template <typename IN_T, bool SPLIT, int DIM, int MB, int NB, int WAVES>
+template <typename IN_T, bool SPLIT, int DIM, int MB, int NB, int R, int WAVES>
 static hipError_t launch_mm_cfg(const FwdParams& p, hipStream_t stream) {
   constexpr int NT = 4 * NB * DIM;
   constexpr int ROWS = MB * DIM;
@@ -540,19 +587,23 @@ static hipError_t launch_mm_cfg(const FwdParams& p, hipStream_t stream) {
   const bool vec = (reinterpret_cast<uintptr_t>(p.x) % 16 == 0) && (reinterpret_cast<uintptr_t>(p.w) % 16 == 0) &&
                    (p.in % per == 0) && (p.x_pop_stride % per == 0);
   if (vec)
-    forward_mm_kernel<IN_T, SPLIT, DIM, MB, NB, WAVES, true><<<grid, 256, 0, stream>>>(p, n_tiles);
+    forward_mm_kernel<IN_T, SPLIT, DIM, MB, NB, R, WAVES, true><<<grid, 256, 0, stream>>>(p, n_tiles);
   else
-    forward_mm_kernel<IN_T, SPLIT, DIM, MB, NB, WAVES, false><<<grid, 256, 0, stream>>>(p, n_tiles);
+    forward_mm_kernel<IN_T, SPLIT, DIM, MB, NB, R, WAVES, false><<<grid, 256, 0, stream>>>(p, n_tiles);
   return hipGetLastError();
 }
 
 template <typename IN_T, bool SPLIT>
 static hipError_t launch_mm_dtype(const FwdParams& p, hipStream_t stream) {
-  if (p.batch <= 16) return launch_mm_cfg<IN_T, SPLIT, 16, 1, 2, 2>(p, stream);
-  if (p.batch <= 32) return launch_mm_cfg<IN_T, SPLIT, 32, 1, 2, 2>(p, stream);
-  if (p.batch <= 64) return launch_mm_cfg<IN_T, SPLIT, 32, 2, 2, 2>(p, stream);
-  if (p.batch <= 128) return launch_mm_cfg<IN_T, SPLIT, 32, 4, 1, 2>(p, stream);
-  return launch_mm_cfg<IN_T, SPLIT, 32, 8, 1, 2>(p, stream);
+  // <DIM, MB row blocks, NB column blocks per wave, R k per lane per chunk,
+  //  waves per SIMD>, chosen by measurement on MI355X.
+  if (p.batch <= 16) return launch_mm_cfg<IN_T, SPLIT, 16, 1, 1, 16, 4>(p, stream);
+  if (p.batch <= 32) return launch_mm_cfg<IN_T, SPLIT, 32, 1, 1, 32, 3>(p, stream);
+  if (p.batch <= 64) return launch_mm_cfg<IN_T, SPLIT, 32, 2, 2, 16, 2>(p, stream);
+  if (p.batch <= 128) return launch_mm_cfg<IN_T, SPLIT, 32, 4, 1, 16, 2>(p, stream);
+  // 256 rows per workgroup; larger batches take several row tiles (grid.y),
+  // each regenerating the same noise.
+  return launch_mm_cfg<IN_T, SPLIT, 32, 8, 1, 16, 2>(p, stream);
 }
 
 // WAVES: waves per SIMD the register allocation must allow.

@@ -92,6 +92,63 @@ __global__ __launch_bounds__(kThreads) void p_hash(uint32_t* out, int iters, uin
   out[g] = acc;
 }
 
+// MFMA / VALU co-execution: per loop slot, one MFMA (or none) and NV integer
+// multiplies on 8 independent chains; 2 waves per SIMD.  If a shape's MFMAs
+// run beside the VALU, slot cycles stay near the VALU-only figure.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+template <int SHAPE, int NV>
+__global__ __launch_bounds__(kThreads) void p_coexec(uint32_t* out, int iters, uint32_t seed) {
+  f32x16 A0 = {}, A1 = {};
+  f32x4 B0 = {}, B1 = {};
+  const float a = threadIdx.x * 1e-3f, b = 1.0001f;
+  bf16x8 ab, bb;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ab[e] = static_cast<__bf16>(threadIdx.x * 1e-3f + e);
+    bb[e] = static_cast<__bf16>(1.0f + e * 1e-2f);
+  }
+  uint32_t v[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) v[c] = threadIdx.x + c + seed;
+  const uint32_t m = 0x9E3779B9u;
+  for (int it = 0; it < iters; ++it) {
+#define VN_PROBE_MFMA(ACC32, ACC16)                                                                              \
+    if (SHAPE == 1) asm volatile("v_mfma_f32_32x32x2_f32 %0, %1, %2, %0" : "+v"(ACC32) : "v"(a), "v"(b));       \
+    if (SHAPE == 2) asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, %0" : "+v"(ACC16) : "v"(a), "v"(b));       \
+    if (SHAPE == 3) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(ACC32) : "v"(ab), "v"(bb));   \
+    if (SHAPE == 4) asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(ACC16) : "v"(ab), "v"(bb));
+    VN_PROBE_MFMA(A0, B0)
+#pragma unroll
+    for (int r = 0; r < NV / 8; ++r)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) asm volatile("v_mul_lo_u32 %0, %0, %1" : "+v"(v[c]) : "v"(m));
+    VN_PROBE_MFMA(A1, B1)
+#pragma unroll
+    for (int r = 0; r < NV / 8; ++r)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) asm volatile("v_mul_lo_u32 %0, %0, %1" : "+v"(v[c]) : "v"(m));
+#undef VN_PROBE_MFMA
+  }
+  float sacc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sacc += A0[i] + A1[i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sacc += B0[i] + B1[i];
+  uint32_t x = 0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) x ^= v[c];
+  out[blockIdx.x * kThreads + threadIdx.x] = x ^ __builtin_bit_cast(uint32_t, sacc);
+}
+
+struct CoProbe {
+  const char* name;
+  void (*fn)(uint32_t*, int, uint32_t);
+  int nv;
+};
+
 struct Probe {
   const char* name;
   void (*fn)(uint32_t*, int, uint32_t);
@@ -158,6 +215,36 @@ int main(int argc, char** argv) {
       std::printf("{\"probe\": \"%s\", \"ms\": %.4f, \"lane_ops_per_s\": %.4e, \"rate_vs_full\": %.3f}\n", pr.name,
                   best, rate, rate / peak_lane_ops);
     }
+    std::fflush(stdout);
+  }
+  // co-execution: 2 waves per SIMD, cycles per slot = SIMD cycles / (slots per wave * waves per SIMD)
+  const CoProbe co[] = {
+      {"none", p_coexec<0, 16>, 16},           {"v_mfma_f32_32x32x2_f32", p_coexec<1, 0>, 0},
+      {"v_mfma_f32_32x32x2_f32", p_coexec<1, 16>, 16}, {"v_mfma_f32_16x16x4_f32", p_coexec<2, 0>, 0},
+      {"v_mfma_f32_16x16x4_f32", p_coexec<2, 16>, 16}, {"v_mfma_f32_32x32x16_bf16", p_coexec<3, 0>, 0},
+      {"v_mfma_f32_32x32x16_bf16", p_coexec<3, 16>, 16}, {"v_mfma_f32_16x16x32_bf16", p_coexec<4, 0>, 0},
+      {"v_mfma_f32_16x16x32_bf16", p_coexec<4, 16>, 16},
+  };
+  const int co_blocks = cus * 2;   // 2 blocks of 4 waves per CU = 2 waves per SIMD
+  const int co_iters = 10000;
+  for (const CoProbe& pr : co) {
+    pr.fn<<<co_blocks, kThreads>>>(out, co_iters / 8, 1u);
+    CHECK(hipGetLastError());
+    CHECK(hipDeviceSynchronize());
+    float best = 1e30f;
+    for (int rep = 0; rep < 3; ++rep) {
+      CHECK(hipEventRecord(e0));
+      pr.fn<<<co_blocks, kThreads>>>(out, co_iters, 2u + rep);
+      CHECK(hipEventRecord(e1));
+      CHECK(hipEventSynchronize(e1));
+      float ms = 0;
+      CHECK(hipEventElapsedTime(&ms, e0, e1));
+      if (ms < best) best = ms;
+    }
+    const double simd_cycles = best * 1e-3 * clock_khz * 1e3;
+    const double slots_per_simd = 2.0 * co_iters * 2.0;  // 2 slots per iteration, 2 waves per SIMD
+    std::printf("{\"coexec\": \"%s\", \"v_mul_lo_u32_per_slot\": %d, \"ms\": %.4f, \"simd_cycles_per_slot\": %.2f}\n",
+                pr.name, pr.nv, best, simd_cycles / slots_per_simd);
     std::fflush(stdout);
   }
   CHECK(hipFree(out));
