@@ -4,8 +4,8 @@ Everything here follows the EvoX API documentation page
 ``evox.triton_kernels.kernels.virtual_noise`` and is written for a reader to
 check against it by eye: integers are ``numpy.uint64`` (products wrap mod
 2**64), floating point is float64 from the exact input values, and the noise
-is materialized per individual exactly as the page's CPU fallback does (entry
-``virtual_perturbed_linear``: "generated per-individual").
+is materialized one individual at a time, as the page's entry
+``virtual_perturbed_linear`` says its CPU fallback does.
 
 Readings of the page (where it is silent or loose) that fix the bit patterns:
 

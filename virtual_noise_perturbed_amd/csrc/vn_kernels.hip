@@ -598,7 +598,7 @@ static hipError_t launch_mm_dtype(const FwdParams& p, hipStream_t stream) {
   // <DIM, MB row blocks, NB column blocks per wave, R k per lane per chunk,
   //  waves per SIMD>, chosen by measurement on MI355X.
   if (p.batch <= 16) return launch_mm_cfg<IN_T, SPLIT, 16, 1, 1, 16, 4>(p, stream);
-  if (p.batch <= 32) return launch_mm_cfg<IN_T, SPLIT, 32, 1, 1, 32, 3>(p, stream);
+  if (p.batch <= 32) return launch_mm_cfg<IN_T, SPLIT, 32, 1, 1, 16, 4>(p, stream);
   if (p.batch <= 64) return launch_mm_cfg<IN_T, SPLIT, 32, 2, 2, 16, 2>(p, stream);
   if (p.batch <= 128) return launch_mm_cfg<IN_T, SPLIT, 32, 4, 1, 16, 2>(p, stream);
   // 256 rows per workgroup; larger batches take several row tiles (grid.y),
