@@ -28,6 +28,13 @@ CASES = [
     (2, 64, 1000, 33, "bf16", True, True, 1 << 33),
     (3, 130, 72, 50, "bf16", True, False, 4),
     (2, 260, 48, 20, "bf16", False, False, 1),
+    # narrow outputs: 16-wide column tiles, waves past `out` idle
+    (4, 64, 256, 10, "f32", True, False, 266752),   # the 256->10 layer shape
+    (3, 50, 100, 16, "bf16", True, False, 6),       # out exactly one 16-wide block, k tail
+    (3, 40, 64, 17, "f32", False, False, 0),        # one past a 16-wide block
+    (2, 64, 96, 128, "bf16", True, True, 12),       # single-column-block tile, full width
+    (2, 60, 72, 129, "f32", True, False, 3),        # two-block tile, second tile mostly idle
+    (5, 20, 40, 3, "f32", True, False, 1),          # 32-row tile, out 3
 ]
 
 

@@ -501,32 +501,40 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
     }
   };
 
+  // A wave whose columns all lie past `out` (narrow layers) only helps stage
+  // X and joins the barriers: no noise, no matrix work.
+  const bool live = jbase < out;
+
   if (nchunks > 0) {
     load_x(0, nfull == 0);
     store_x(0);
-    load_w(0, nfull == 0);
+    if (live) {
+      load_w(0, nfull == 0);
+      float nz[NB][R];
+      make_noise(nz);
+      make_b(nz, 0, nfull == 0);
+    }
     if (nchunks > 1) load_x(1, nfull <= 1);
-    float nz[NB][R];
-    make_noise(nz);
-    make_b(nz, 0, nfull == 0);
   }
   __syncthreads();
   // Steady state: chunks c+1 and c+2 are whole, nothing is guarded.
   int64_t c = 0;
   for (; c + 2 < nfull; ++c) {
     store_x(static_cast<int>((c + 1) & 1));
-    load_w(c + 1, false);
     load_x(c + 2, false);
-    float nz[NB][R];
-    make_noise(nz);
-    multiply(static_cast<int>(c & 1));
-    make_b(nz, c + 1, false);
-    // Interleave: one MFMA, then a share of the noise VALU work, repeatedly,
-    // so the matrix cores run under the hash instead of after it.
+    if (live) {
+      load_w(c + 1, false);
+      float nz[NB][R];
+      make_noise(nz);
+      multiply(static_cast<int>(c & 1));
+      make_b(nz, c + 1, false);
+      // Interleave: one MFMA, then a share of the noise VALU work, repeatedly,
+      // so the matrix cores run under the hash instead of after it.
 #pragma unroll
-    for (int k = 0; k < kMfmaPerChunk; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+      for (int k = 0; k < kMfmaPerChunk; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+      }
     }
     __syncthreads();
   }
@@ -535,13 +543,13 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
     const bool next = c + 1 < nchunks;
     if (next) {
       store_x(static_cast<int>((c + 1) & 1));
-      load_w(c + 1, c + 1 >= nfull);
+      if (live) load_w(c + 1, c + 1 >= nfull);
       if (c + 2 < nchunks) load_x(c + 2, c + 2 >= nfull);
     }
     float nz[NB][R];
-    if (next) make_noise(nz);
-    multiply(static_cast<int>(c & 1));
-    if (next) make_b(nz, c + 1, c + 1 >= nfull);
+    if (next && live) make_noise(nz);
+    if (live) multiply(static_cast<int>(c & 1));
+    if (next && live) make_b(nz, c + 1, c + 1 >= nfull);
     __syncthreads();
   }
 
@@ -598,7 +606,11 @@ static hipError_t launch_mm_dtype(const FwdParams& p, hipStream_t stream) {
   // <DIM, MB row blocks, NB column blocks per wave, R k per lane per chunk,
   //  waves per SIMD>, chosen by measurement on MI355X.
   if (p.batch <= 16) return launch_mm_cfg<IN_T, SPLIT, 16, 1, 1, 16, 4>(p, stream);
+  // Narrow outputs: 16-wide column blocks waste the least noise work on
+  // columns past `out` (whole waves past it are skipped in the kernel).
+  if (p.out <= 16 && p.batch <= 64) return launch_mm_cfg<IN_T, SPLIT, 16, 4, 1, 16, 2>(p, stream);
   if (p.batch <= 32) return launch_mm_cfg<IN_T, SPLIT, 32, 1, 1, 16, 4>(p, stream);
+  if (p.batch <= 64 && p.out <= 128) return launch_mm_cfg<IN_T, SPLIT, 32, 2, 1, 16, 2>(p, stream);
   if (p.batch <= 64) return launch_mm_cfg<IN_T, SPLIT, 32, 2, 2, 16, 2>(p, stream);
   if (p.batch <= 128) return launch_mm_cfg<IN_T, SPLIT, 32, 4, 1, 16, 2>(p, stream);
   // 256 rows per workgroup; larger batches take several row tiles (grid.y),
