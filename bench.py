@@ -122,10 +122,26 @@ class Step:
         # outputs preallocated so the step does no allocation
         self.ys = [torch.empty((wl.pop, wl.batch, L.out_features), dtype=torch.float32, device=device)
                    for L in wl.layers]
-        self.gws = [torch.empty(L.out_features * L.in_features, dtype=torch.float32, device=device)
-                    for L in wl.layers]
-        self.gbs = [None if L.bias is None else torch.empty(L.out_features, dtype=torch.float32, device=device)
-                    for L in wl.layers]
+        # Gradient blocks.  When the parameter blocks tile one flat range of
+        # noise offsets (weights then bias of each layer, layer after layer),
+        # the whole gradient is one launch over that range and each block is a
+        # view of it; otherwise one launch per block.
+        blocks = []
+        for L in wl.layers:
+            blocks.append((L.w_offset, L.out_features * L.in_features))
+            if L.bias is not None:
+                blocks.append((L.b_offset, L.out_features))
+        blocks.sort()
+        self.flat_base = blocks[0][0]
+        self.flat_n = sum(n for _, n in blocks)
+        self.flat = all(blocks[k][0] + blocks[k][1] == blocks[k + 1][0] for k in range(len(blocks) - 1))
+        if self.flat:
+            self.gflat = torch.empty(self.flat_n, dtype=torch.float32, device=device)
+            view = lambda off, n: self.gflat[off - self.flat_base: off - self.flat_base + n]
+        else:
+            view = lambda off, n: torch.empty(n, dtype=torch.float32, device=device)
+        self.gws = [view(L.w_offset, L.out_features * L.in_features) for L in wl.layers]
+        self.gbs = [None if L.bias is None else view(L.b_offset, L.out_features) for L in wl.layers]
 
     def forward_only(self, math):
         """Forward of every layer in the given math mode (for a side measurement)."""
@@ -138,14 +154,24 @@ class Step:
                                         out=self.ys[li], math=math)
             h = self.ys[li]
 
-    def gradients_only(self):
+    def gradient_launches(self):
+        """(name, fn) for each gradient launch of the step."""
         wl, vn = self.wl, self.vn
+        if self.flat:
+            return [("grad_flat", lambda: vn.virtual_flat_gradient(
+                self.fit, self.seeds, self.flat_n, wl.sigma, wl.pop, self.flat_base, out=self.gflat))]
+        out = []
         for li, (L, w, b) in enumerate(self.layers):
-            vn.virtual_flat_gradient(self.fit, self.seeds, L.out_features * L.in_features, wl.sigma, wl.pop,
-                                     L.w_offset, out=self.gws[li])
+            out.append((f"grad_w{li}", lambda L=L, g=self.gws[li]: vn.virtual_flat_gradient(
+                self.fit, self.seeds, L.out_features * L.in_features, wl.sigma, wl.pop, L.w_offset, out=g)))
             if b is not None:
-                vn.virtual_flat_gradient(self.fit, self.seeds, L.out_features, wl.sigma, wl.pop, L.b_offset,
-                                         out=self.gbs[li])
+                out.append((f"grad_b{li}", lambda L=L, g=self.gbs[li]: vn.virtual_flat_gradient(
+                    self.fit, self.seeds, L.out_features, wl.sigma, wl.pop, L.b_offset, out=g)))
+        return out
+
+    def gradients_only(self):
+        for _, fn in self.gradient_launches():
+            fn()
 
     def run(self, events=None):
         """events: optional list to which (name, start_event, end_event) are appended."""
@@ -170,12 +196,8 @@ class Step:
             timed(f"forward{li}", lambda h=h, w=w, b=b, L=L, y=y, act=act: vn.virtual_perturbed_linear(
                 h, w, b, self.seeds, wl.sigma, L.w_offset, activation=act, out=y))
             h = y
-        for li, (L, w, b) in enumerate(self.layers):
-            timed(f"grad_w{li}", lambda L=L, g=self.gws[li]: vn.virtual_flat_gradient(
-                self.fit, self.seeds, L.out_features * L.in_features, wl.sigma, wl.pop, L.w_offset, out=g))
-            if b is not None:
-                timed(f"grad_b{li}", lambda L=L, g=self.gbs[li]: vn.virtual_flat_gradient(
-                    self.fit, self.seeds, L.out_features, wl.sigma, wl.pop, L.b_offset, out=g))
+        for name, fn in self.gradient_launches():
+            timed(name, fn)
 
 
 def copy_calibration(torch, device):
@@ -308,14 +330,16 @@ def main():
 
     # dominant kernel: the launch with the largest average duration
     dom = max(avg_ms, key=avg_ms.get)
-    li = int(dom[-1])
-    L = wl.layers[li]
-    if dom.startswith("forward"):
-        units = wl.pop * (L.out_features * L.in_features + (L.out_features if L.bias is not None else 0))
-    elif dom.startswith("grad_w"):
-        units = wl.pop * L.out_features * L.in_features
+    if dom == "grad_flat":
+        units = wl.pop * step.flat_n
     else:
-        units = wl.pop * L.out_features
+        L = wl.layers[int(dom[-1])]
+        if dom.startswith("forward"):
+            units = wl.pop * (L.out_features * L.in_features + (L.out_features if L.bias is not None else 0))
+        elif dom.startswith("grad_w"):
+            units = wl.pop * L.out_features * L.in_features
+        else:
+            units = wl.pop * L.out_features
     achieved = units / (avg_ms[dom] * 1e-3)
     traffic = recorded_traffic(args.workload, dom)
     roofline = {

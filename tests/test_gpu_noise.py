@@ -73,6 +73,26 @@ def test_forward_readout(mode, fin, fout):
     assert np.array_equal(y.astype(np.float64), want)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_forward_readout_tiny_sigma(dt):
+    """sigma = 2^-101: sigma * 2^-24 is subnormal, so the call takes the kernels
+    that form sigma * N in floating point; X = I, W = 0 reads back sigma * N
+    (exact in fp32, rounded once to bf16 for bf16 operands)."""
+    dev = device()
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    fin, fout, offset = 40, 24, 77
+    seeds = np.array([3, -9], dtype=np.int64)
+    sigma = 2.0 ** -101
+    x = torch.eye(fin, dtype=dtype, device=dev)
+    w = torch.zeros((fout, fin), dtype=dtype, device=dev)
+    y = vn.virtual_perturbed_linear(x, w, None, to_dev(seeds), sigma, offset).cpu().numpy()
+    n = oracle.noise(seeds, fout * fin, offset).reshape(2, fout, fin)
+    want = np.transpose(n, (0, 2, 1)) * sigma
+    if dt == "bf16":
+        want = bf16_round_cpu(want)
+    assert np.array_equal(y.astype(np.float64), want)
+
+
 def test_forward_bias_readout():
     """X = 0, W = 0, b = 0, sigma = 1: Y[i, b, j] = nb_i[j] at offset + out*in + j."""
     dev = device()

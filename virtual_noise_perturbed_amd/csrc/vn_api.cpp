@@ -161,12 +161,19 @@ int vn_perturbed_linear(const void* x, int64_t x_pop_stride, const void* w, int3
   p.in = in;
   p.out = out;
   p.sigma = sigma;
+  p.sigma_q = sigma * 0x1p-24f;
   p.offset = offset;
   p.relu = activation == VN_ACT_RELU;
   p.y = y;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == VN_BF16) return hip_status(vn::launch_forward_bf16(p, s));
-  return hip_status(math == VN_MATH_F32 ? vn::launch_forward_f32_exact(p, s) : vn::launch_forward_f32(p, s));
+  // The fast kernels scale the integer noise by sigma * 2^-24, exact unless it
+  // falls below the normal range; such a sigma takes the kernels that form
+  // sigma * N in floating point.
+  const bool tiny_sigma = sigma != 0.0f && std::fabs(sigma) < 0x1p-100f;
+  if (dtype == VN_BF16)
+    return hip_status(tiny_sigma ? vn::launch_forward_bf16_exact(p, s) : vn::launch_forward_bf16(p, s));
+  return hip_status(math == VN_MATH_F32 || tiny_sigma ? vn::launch_forward_f32_exact(p, s)
+                                                       : vn::launch_forward_f32(p, s));
 }
 
 int vn_flat_gradient(const float* fitness, const void* seeds, int32_t seed_dtype, int64_t pop_size, int64_t n,

@@ -20,15 +20,62 @@ namespace vn {
 
 // API data entry _SPLITMIX64_GAMMA = 11400714819323198485.
 constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+constexpr uint32_t kGammaLo = static_cast<uint32_t>(kGamma);
+constexpr uint32_t kGammaHi = static_cast<uint32_t>(kGamma >> 32);
 
 // (idx + 1) * GAMMA for a compile-time step count.
 __host__ __device__ constexpr uint64_t gamma_times(uint64_t t) { return t * kGamma; }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// t * GAMMA mod 2^64 on 32-bit words.  The two cross products only matter
+// mod 2^32, so the second one takes the first as the addend of a 32x32->64
+// multiply-add (whose high word is left arbitrary), and their sum enters the
+// low product as the high word of its addend: three multiplies and a move,
+// where the plain 64-bit product costs two multiply-lows, a multiply-add and
+// a three-way add.
+__device__ __forceinline__ uint64_t mul_gamma(uint64_t t) {
+  const uint32_t lo = static_cast<uint32_t>(t), hi = static_cast<uint32_t>(t >> 32);
+  u32x2 c;
+  c.x = lo * kGammaHi;
+  c.y = __builtin_nondeterministic_value(c.x);
+  const uint32_t cross = static_cast<uint32_t>(static_cast<uint64_t>(hi) * kGammaLo + __builtin_bit_cast(uint64_t, c));
+  return static_cast<uint64_t>(lo) * kGammaLo + (static_cast<uint64_t>(cross) << 32);
+}
+
+// Finalizer rounds on the state, up to the last product (still 64-bit).
+__device__ __forceinline__ uint64_t mix_rounds(uint64_t z) {
+  z = mul_gamma(z ^ (z >> 30));
+  z = mul_gamma(z ^ (z >> 27));
+#if defined(__HIP_DEVICE_COMPILE__)
+  // Use the product's words as computed: without this the compiler
+  // recomputes the low word with a separate multiply.
+  asm("" : "+v"(z));
+#endif
+  return z;
+}
+
 // 64-bit state -> low 32 bits of the finalizer output.
 __device__ __forceinline__ uint32_t mix_lo32(uint64_t z) {
-  z = (z ^ (z >> 30)) * kGamma;
-  z = (z ^ (z >> 27)) * kGamma;
+  z = mix_rounds(z);
   return static_cast<uint32_t>(z ^ (z >> 31));
+}
+
+// 64-bit state -> (r >> 8) - 2^23 as a signed integer, r the finalizer
+// output: the noise times 2^24, exact in fp32.  Flipping bit 31 of r turns
+// the unsigned shift into an arithmetic one on the centred value; the flip
+// rides on the final xor as a three-way xor (one bitop3, at the xor's rate).
+__device__ __forceinline__ int32_t centered_q(uint64_t z) {
+  z = mix_rounds(z);
+  const uint32_t lo = static_cast<uint32_t>(z), hi = static_cast<uint32_t>(z >> 32);
+  const uint32_t sh = __builtin_amdgcn_alignbit(hi, lo, 31);   // low word of z >> 31
+  uint32_t r;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(lo), "v"(sh), "s"(0x80000000u));
+#else
+  r = lo ^ sh ^ 0x80000000u;
+#endif
+  return static_cast<int32_t>(r) >> 8;
 }
 
 // Initial state of element `idx` (absolute flat index) for seed `s`.

@@ -314,7 +314,11 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
   constexpr int PLANES = SPLIT ? 2 : 1;
   constexpr int PLANE = ROWS * STRIDE;
   constexpr int BUF = PLANES * PLANE;
-  constexpr int SEG_PER_ROW = KC / 8;                 // a segment is 8 consecutive k of one row
+  // A segment is SEGK consecutive k of one X row: 8, or 4 for fp32 when the
+  // tile has fewer than 256 eight-wide segments (so no thread repeats one).
+  constexpr int SEGK = (sizeof(IN_T) == 4 && ROWS * KC / 8 < 256) ? 4 : 8;
+  constexpr int SEG_LOADS = SEGK * static_cast<int>(sizeof(IN_T)) / 16;   // 16-byte loads per segment
+  constexpr int SEG_PER_ROW = KC / SEGK;
   constexpr int NSEG = ROWS * SEG_PER_ROW;
   constexpr int SEG_PER_THREAD = (NSEG + 255) / 256;
   constexpr uint64_t kChunkStep = gamma_times(KC);
@@ -357,8 +361,8 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
   }
 
   // ---- A side: this thread's segments of the X tile.  Segment q covers row
-  // q / SEG_PER_ROW and k = (q % SEG_PER_ROW) * 8 .. + 8 of the chunk.  Rows
-  // past `batch` read the last row: they only feed discarded outputs.
+  // q / SEG_PER_ROW and k = (q % SEG_PER_ROW) * SEGK .. + SEGK of the chunk.
+  // Rows past `batch` read the last row: they only feed discarded outputs.
   const IN_T* xsrc[SEG_PER_THREAD];
   int xdst[SEG_PER_THREAD];
 #pragma unroll
@@ -368,13 +372,13 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
     // the pipelined loop free of branches.
     const int q = (tid + u * 256) % NSEG;
     const int row = q / SEG_PER_ROW;
-    const int kk = (q % SEG_PER_ROW) * 8;
+    const int kk = (q % SEG_PER_ROW) * SEGK;
     int64_t b = m0 + row;
     b = b < batch ? b : batch - 1;
     xsrc[u] = xi + b * in + kk;
     xdst[u] = row * STRIDE + kk;
   }
-  IN_T xs[SEG_PER_THREAD][8];
+  IN_T xs[SEG_PER_THREAD][SEGK];
   auto load_x = [&](int64_t c, bool guarded) {
     const int64_t k0 = c * KC;
 #pragma unroll
@@ -382,7 +386,7 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
       const IN_T* src = xsrc[u] + k0;
       if (!guarded) {
 #pragma unroll
-        for (int h = 0; h < static_cast<int>(8 * sizeof(IN_T) / 16); ++h) {
+        for (int h = 0; h < SEG_LOADS; ++h) {
           const uint4 v = *reinterpret_cast<const uint4*>(src + h * (16 / sizeof(IN_T)));
           __builtin_memcpy(&xs[u][h * (16 / sizeof(IN_T))], &v, 16);
         }
@@ -390,29 +394,34 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
         const int64_t kmax = in - (k0 + (xdst[u] % STRIDE));   // valid k left in this segment
         // (xdst % STRIDE is the segment's k offset within the chunk)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xs[u][e] = (e < kmax) ? src[e] : static_cast<IN_T>(0.0f);
+        for (int e = 0; e < SEGK; ++e) xs[u][e] = (e < kmax) ? src[e] : static_cast<IN_T>(0.0f);
       }
     }
   };
   auto store_x = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < SEG_PER_THREAD; ++u) {
-      uint4 hi, lo;
       if constexpr (sizeof(IN_T) == 2) {
-        __builtin_memcpy(&hi, &xs[u][0], 16);   // bf16 operands go to LDS as they are
+        uint4 v;
+        __builtin_memcpy(&v, &xs[u][0], 16);   // bf16 operands go to LDS as they are
+        *reinterpret_cast<uint4*>(&lds[buf * BUF + xdst[u]]) = v;
       } else {
-        uint32_t hw[4], lw[4];
+        using Packed = std::conditional_t<SEGK == 8, uint4, uint2>;   // SEGK bf16 values
+        uint32_t hw[SEGK / 2], lw[SEGK / 2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < SEGK / 2; ++e) {
           const float a = to_f32(xs[u][2 * e]), b = to_f32(xs[u][2 * e + 1]);
           hw[e] = pack_bf16x2(a, b);
           if constexpr (SPLIT) lw[e] = pack_bf16x2(a - bf16_lo_to_f32(hw[e]), b - bf16_hi_to_f32(hw[e]));
         }
-        __builtin_memcpy(&hi, hw, 16);
-        if constexpr (SPLIT) __builtin_memcpy(&lo, lw, 16);
+        Packed hi, lo;
+        __builtin_memcpy(&hi, hw, sizeof(Packed));
+        *reinterpret_cast<Packed*>(&lds[buf * BUF + xdst[u]]) = hi;
+        if constexpr (SPLIT) {
+          __builtin_memcpy(&lo, lw, sizeof(Packed));
+          *reinterpret_cast<Packed*>(&lds[buf * BUF + PLANE + xdst[u]]) = lo;
+        }
       }
-      *reinterpret_cast<uint4*>(&lds[buf * BUF + xdst[u]]) = hi;
-      if constexpr (SPLIT) *reinterpret_cast<uint4*>(&lds[buf * BUF + PLANE + xdst[u]]) = lo;
     }
   };
 
@@ -442,14 +451,16 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
       for (int nb = 0; nb < NB; ++nb) load_run_guarded<IN_T, R>(wv[nb], wrow[nb] + c * KC, valid);
     }
   };
-  // Noise of chunk c (the lane's runs; consecutive k step the state by +GAMMA).
+  // Noise of chunk c (the lane's runs; consecutive k step the state by +GAMMA),
+  // as the integers N * 2^24 (exact in fp32); sigma_q = sigma * 2^-24 scales
+  // them back inside the fma of make_b.
   auto make_noise = [&](float (&nz)[NB][R]) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       uint64_t zt = z[nb];
 #pragma unroll
       for (int t = 0; t < R; ++t) {
-        nz[nb][t] = noise_of_state(zt);
+        nz[nb][t] = static_cast<float>(centered_q(zt));
         zt += kGamma;
       }
       z[nb] += kChunkStep;
@@ -466,8 +477,8 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
       for (int e = 0; e < R / 2; ++e) {
-        float a = __builtin_fmaf(p.sigma, nz[nb][2 * e], to_f32(wv[nb][2 * e]));
-        float b = __builtin_fmaf(p.sigma, nz[nb][2 * e + 1], to_f32(wv[nb][2 * e + 1]));
+        float a = __builtin_fmaf(p.sigma_q, nz[nb][2 * e], to_f32(wv[nb][2 * e]));
+        float b = __builtin_fmaf(p.sigma_q, nz[nb][2 * e + 1], to_f32(wv[nb][2 * e + 1]));
         if (guarded) {
           a = (2 * e < valid) ? a : 0.0f;
           b = (2 * e + 1 < valid) ? b : 0.0f;
@@ -610,8 +621,7 @@ static hipError_t launch_mm_dtype(const FwdParams& p, hipStream_t stream) {
   // columns past `out` (whole waves past it are skipped in the kernel).
   if (p.out <= 16 && p.batch <= 64) return launch_mm_cfg<IN_T, SPLIT, 16, 4, 1, 16, 2>(p, stream);
   if (p.batch <= 32) return launch_mm_cfg<IN_T, SPLIT, 32, 1, 1, 16, 4>(p, stream);
-  if (p.batch <= 64 && p.out <= 128) return launch_mm_cfg<IN_T, SPLIT, 32, 2, 1, 16, 2>(p, stream);
-  if (p.batch <= 64) return launch_mm_cfg<IN_T, SPLIT, 32, 2, 2, 16, 2>(p, stream);
+  if (p.batch <= 64) return launch_mm_cfg<IN_T, SPLIT, 32, 2, 1, 16, 4>(p, stream);
   if (p.batch <= 128) return launch_mm_cfg<IN_T, SPLIT, 32, 4, 1, 16, 2>(p, stream);
   // 256 rows per workgroup; larger batches take several row tiles (grid.y),
   // each regenerating the same noise.
@@ -663,10 +673,15 @@ hipError_t launch_forward_f32_exact(const FwdParams& p, hipStream_t stream) {
 hipError_t launch_forward_bf16(const FwdParams& p, hipStream_t stream) {
   return launch_mm_dtype<__bf16, false>(p, stream);
 }
+hipError_t launch_forward_bf16_exact(const FwdParams& p, hipStream_t stream) {
+  return launch_fwd_cfg<__bf16, 32, 8, 1, 1, 2>(p, stream);
+}
 
 // ---------------------------------------------------------------------------
 // Gradient, element-major: grad[t] = scale * sum_i f_i noise_i[offset + t].
 // Lane owns E consecutive elements; wave w walks its quarter of the population.
+// The sums run over the integers N * 2^24 and take the 2^-24 at the end: a
+// power-of-two factor, so every rounding is the one of the sum over N.
 template <int E>
 __global__ __launch_bounds__(256) void grad_elem_kernel(GradParams p, int64_t n_blocks) {
   __shared__ float red[4][64 * E];
@@ -694,14 +709,14 @@ __global__ __launch_bounds__(256) void grad_elem_kernel(GradParams p, int64_t n_
         const uint64_t s = load_seed(p.seeds, p.seeds_i32, i + u);
         const float f = p.fitness[i + u];
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(f, noise_of_state(s + c[e]), acc[e]);
+        for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(f, static_cast<float>(centered_q(s + c[e])), acc[e]);
       }
     }
     for (; i < i_end; ++i) {
       const uint64_t s = load_seed(p.seeds, p.seeds_i32, i);
       const float f = p.fitness[i];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(f, noise_of_state(s + c[e]), acc[e]);
+      for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(f, static_cast<float>(centered_q(s + c[e])), acc[e]);
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) red[wave][lane * E + e] = acc[e];
@@ -711,7 +726,7 @@ __global__ __launch_bounds__(256) void grad_elem_kernel(GradParams p, int64_t n_
       for (int e = 0; e < E; ++e) {
         const int k = lane * E + e;
         const float v = ((red[0][k] + red[1][k]) + red[2][k]) + red[3][k];
-        if (e0 + e < p.n) p.out[e0 + e] = v * p.scale;
+        if (e0 + e < p.n) p.out[e0 + e] = (v * 0x1p-24f) * p.scale;
       }
     }
     __syncthreads();
@@ -727,10 +742,10 @@ __global__ __launch_bounds__(256) void grad_pop_kernel(GradParams p) {
     const uint64_t c = state_of(0, static_cast<uint64_t>(p.offset + t));
     float acc = 0.0f;
     for (int64_t i = lane; i < p.pop; i += 64)
-      acc = __builtin_fmaf(p.fitness[i], noise_of_state(load_seed(p.seeds, p.seeds_i32, i) + c), acc);
+      acc = __builtin_fmaf(p.fitness[i], static_cast<float>(centered_q(load_seed(p.seeds, p.seeds_i32, i) + c)), acc);
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, 64);
-    if (lane == 0) p.out[t] = acc * p.scale;
+    if (lane == 0) p.out[t] = (acc * 0x1p-24f) * p.scale;
   }
 }
 

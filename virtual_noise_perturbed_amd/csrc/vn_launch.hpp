@@ -16,6 +16,7 @@ struct FwdParams {
   bool seeds_i32;
   int64_t pop, batch, in, out;
   float sigma;
+  float sigma_q;         // sigma * 2^-24 (exact): multiplier of the integer noise (r >> 8) - 2^23
   int64_t offset;
   bool relu;
   float* y;
@@ -36,6 +37,9 @@ struct GradParams {
 hipError_t launch_forward_f32(const FwdParams& p, hipStream_t stream);        // split-bf16 matrix cores
 hipError_t launch_forward_f32_exact(const FwdParams& p, hipStream_t stream);  // fp32 matrix cores
 hipError_t launch_forward_bf16(const FwdParams& p, hipStream_t stream);
+// bf16 operands with the noise formed in floating point (sigma * N): for a
+// sigma too small for sigma * 2^-24 to be a normal float.
+hipError_t launch_forward_bf16_exact(const FwdParams& p, hipStream_t stream);
 hipError_t launch_gradient(const GradParams& p, hipStream_t stream);
 hipError_t launch_noise(const void* seeds, bool seeds_i32, int64_t pop, int64_t n, int64_t offset,
                         uint32_t* r_out, float* n_out, hipStream_t stream);

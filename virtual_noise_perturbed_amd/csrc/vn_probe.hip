@@ -30,14 +30,15 @@
 constexpr int kThreads = 256;
 constexpr int kChains = 16;
 
-// 32-bit ops: a = op(a, b) on 16 chains.
+// 32-bit ops: a = op(a, b[, b2]) on 16 chains.
 #define PROBE32(NAME, ASM)                                                              \
   __global__ __launch_bounds__(kThreads) void NAME(uint32_t* out, int iters, uint32_t seed) { \
     uint32_t a[kChains];                                                                \
     const uint32_t b = seed * 2654435761u + threadIdx.x;                                \
+    const uint32_t b2 = seed ^ (threadIdx.x * 40503u);                                  \
     _Pragma("unroll") for (int c = 0; c < kChains; ++c) a[c] = threadIdx.x + c * 977u + seed; \
     for (int it = 0; it < iters; ++it) {                                                \
-      _Pragma("unroll") for (int c = 0; c < kChains; ++c) asm volatile(ASM : "+v"(a[c]) : "v"(b)); \
+      _Pragma("unroll") for (int c = 0; c < kChains; ++c) asm volatile(ASM : "+v"(a[c]) : "v"(b), "v"(b2)); \
     }                                                                                   \
     uint32_t r = 0;                                                                     \
     _Pragma("unroll") for (int c = 0; c < kChains; ++c) r ^= a[c];                      \
@@ -70,6 +71,14 @@ PROBE32(p_add3, "v_add3_u32 %0, %0, %1, %0")
 PROBE32(p_lshr, "v_lshrrev_b32 %0, 8, %0")
 PROBE32(p_cvt, "v_cvt_f32_u32 %0, %0")
 PROBE32(p_fma, "v_fma_f32 %0, %0, %1, %0")
+PROBE32(p_fmac, "v_fmac_f32 %0, %1, %2")
+PROBE32(p_mov, "v_mov_b32 %0, %1")
+PROBE32(p_xad, "v_xad_u32 %0, %0, %1, %0")
+PROBE32(p_bitop3, "v_bitop3_b32 %0, %0, %1, %0 bitop3:0x96")
+PROBE32(p_ashr, "v_ashrrev_i32 %0, 8, %0")
+PROBE32(p_cvt_i32, "v_cvt_f32_i32 %0, %0")
+PROBE32(p_cvt_ubyte, "v_cvt_f32_ubyte2 %0, %0")
+PROBE32(p_perm, "v_perm_b32 %0, %0, %1, %1")
 PROBE64(p_mad64, "v_mad_u64_u32 %0, vcc, %2, %3, %0")
 PROBE64(p_shr64, "v_lshrrev_b64 %0, 30, %0")
 PROBE64(p_add64, "v_lshl_add_u64 %0, %0, 0, %1")
@@ -86,6 +95,28 @@ __global__ __launch_bounds__(kThreads) void p_hash(uint32_t* out, int iters, uin
 #pragma unroll
     for (int c = 0; c < S; ++c) {
       acc ^= vn::mix_lo32(z[c]);
+      z[c] += vn::gamma_times(S);
+    }
+  }
+  out[g] = acc;
+}
+
+// The same hash written as plain 64-bit C (z * GAMMA), for comparison with
+// the library's word-level form.
+__global__ __launch_bounds__(kThreads) void p_hash_plain(uint32_t* out, int iters, uint32_t seed) {
+  constexpr int S = 8;
+  uint64_t z[S];
+  const uint64_t g = blockIdx.x * kThreads + threadIdx.x;
+#pragma unroll
+  for (int c = 0; c < S; ++c) z[c] = vn::state_of(seed, g * 64 + c);
+  uint32_t acc = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < S; ++c) {
+      uint64_t t = z[c];
+      t = (t ^ (t >> 30)) * vn::kGamma;
+      t = (t ^ (t >> 27)) * vn::kGamma;
+      acc ^= static_cast<uint32_t>(t ^ (t >> 31));
       z[c] += vn::gamma_times(S);
     }
   }
@@ -185,10 +216,19 @@ int main(int argc, char** argv) {
       {"v_lshrrev_b32", p_lshr, kChains, "32-bit"},
       {"v_cvt_f32_u32", p_cvt, kChains, "32-bit"},
       {"v_fma_f32", p_fma, kChains, "32-bit"},
+      {"v_fmac_f32", p_fmac, kChains, "32-bit"},
+      {"v_mov_b32", p_mov, kChains, "32-bit"},
+      {"v_xad_u32", p_xad, kChains, "32-bit"},
+      {"v_bitop3_b32", p_bitop3, kChains, "32-bit"},
+      {"v_ashrrev_i32", p_ashr, kChains, "32-bit"},
+      {"v_cvt_f32_i32", p_cvt_i32, kChains, "32-bit"},
+      {"v_cvt_f32_ubyte2", p_cvt_ubyte, kChains, "32-bit"},
+      {"v_perm_b32", p_perm, kChains, "32-bit"},
       {"v_mad_u64_u32", p_mad64, kChains, "64-bit"},
       {"v_lshrrev_b64", p_shr64, kChains, "64-bit"},
       {"v_lshl_add_u64", p_add64, kChains, "64-bit"},
       {"hash", p_hash, 8, "hash"},
+      {"hash_plain", p_hash_plain, 8, "hash"},
   };
   const double peak_lane_ops = static_cast<double>(cus) * 64.0 * clock_khz * 1e3;
   for (const Probe& pr : probes) {
@@ -209,8 +249,8 @@ int main(int argc, char** argv) {
     const double ops = static_cast<double>(blocks) * kThreads * iters * pr.per_iter;
     const double rate = ops / (best * 1e-3);
     if (std::strcmp(pr.what, "hash") == 0) {
-      std::printf("{\"probe\": \"hash\", \"ms\": %.4f, \"hashes_per_s\": %.4e, \"lane_cycles_per_hash\": %.2f}\n", best,
-                  rate, peak_lane_ops / rate);
+      std::printf("{\"probe\": \"%s\", \"ms\": %.4f, \"hashes_per_s\": %.4e, \"lane_cycles_per_hash\": %.2f}\n", pr.name,
+                  best, rate, peak_lane_ops / rate);
     } else {
       std::printf("{\"probe\": \"%s\", \"ms\": %.4f, \"lane_ops_per_s\": %.4e, \"rate_vs_full\": %.3f}\n", pr.name,
                   best, rate, rate / peak_lane_ops);
