@@ -45,15 +45,16 @@ METRIC = "perturbed-linear TFLOP/s + noise-gradient elements/s, % of roofline, 1
 # this work per element, so it is the peak their rates are compared with.
 N_SIMD = 256 * 4
 CLOCK_HZ = 2.4e9
-PROBE_RATE = {            # measured issue rate, fraction of 64 lane-ops/CU/clk
-    "v_lshl_add_u64": 0.825, "v_lshrrev_b64": 0.854, "v_xor_b32": 1.314,
-    "v_mul_lo_u32": 0.778, "v_mad_u64_u32": 0.791, "v_add3_u32": 0.885,
-    "v_alignbit_b32": 0.893, "v_lshrrev_b32": 1.485, "v_cvt_f32_u32": 0.849,
+PROBE_RATE = {            # measured issue rate, fraction of 64 lane-ops/CU/clk (vn_probe)
+    "v_lshl_add_u64": 0.820, "v_lshrrev_b64": 0.849, "v_xor_b32": 1.273,
+    "v_mul_lo_u32": 0.855, "v_mad_u64_u32": 0.775, "v_mov_b32": 1.419,
+    "v_alignbit_b32": 0.823, "v_bitop3_b32": 1.456, "v_ashrrev_i32": 1.430,
+    "v_cvt_f32_i32": 0.845,
 }
-HASH_ISA = {              # instructions per noise element
-    "v_lshl_add_u64": 1, "v_lshrrev_b64": 2, "v_xor_b32": 5, "v_mul_lo_u32": 4,
-    "v_mad_u64_u32": 2, "v_add3_u32": 2, "v_alignbit_b32": 1, "v_lshrrev_b32": 1,
-    "v_cvt_f32_u32": 1,
+HASH_ISA = {              # instructions per noise element: state step, finalizer, N * 2^24 as fp32
+    "v_lshl_add_u64": 1, "v_lshrrev_b64": 2, "v_xor_b32": 4, "v_mul_lo_u32": 2,
+    "v_mad_u64_u32": 4, "v_mov_b32": 2, "v_alignbit_b32": 1, "v_bitop3_b32": 1,
+    "v_ashrrev_i32": 1, "v_cvt_f32_i32": 1,
 }
 HASH_SIMD_CYCLES = sum(n * 4.0 / PROBE_RATE[k] for k, n in HASH_ISA.items())   # per wave64 element
 HASH_PEAK_PER_S = N_SIMD * 64 * CLOCK_HZ / HASH_SIMD_CYCLES
@@ -90,8 +91,8 @@ def recorded_traffic(workload_key: int, kernel: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
