@@ -99,7 +99,7 @@ def parse():
                     help="approximate CPU seconds for the oracle baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (to scale memory counters)")
-    ap.add_argument("--only", choices=["forward", "gradient"], default=None,
+    ap.add_argument("--only", choices=["forward", "gradient", "metric"], default=None,
                     help="run only one kernel family in the timed steps (for profiling runs)")
     return ap.parse_args()
 
@@ -154,6 +154,22 @@ class Step:
             vn.virtual_perturbed_linear(h, w, b, self.seeds, wl.sigma, L.w_offset, activation=act,
                                         out=self.ys[li], math=math)
             h = self.ys[li]
+
+    def metric_setup(self):
+        """The flat parameter vector (weights then bias of each layer) as the
+        centre of the reduce-metric side measurement."""
+        torch, wl = self.torch, self.wl
+        parts = []
+        for L, w, b in self.layers:
+            parts.append(w.float().reshape(-1))
+            if b is not None:
+                parts.append(b.float())
+        self.center = torch.cat(parts).contiguous()
+        self.metric_out = None
+
+    def metric(self):
+        wl = self.wl
+        self.metric_out = self.vn.virtual_reduce_metric(self.center, self.seeds, wl.sigma, self.center.numel(), 0)
 
     def gradient_launches(self):
         """(name, fn) for each gradient launch of the step."""
@@ -300,9 +316,13 @@ def main():
     step = Step(wl, torch, vn, device)
     if args.only is not None:
         # profiling aid: the timed steps of one kernel family only
+        if args.only == "metric":
+            step.metric_setup()
         for _ in range(args.warmup + args.steps):
             if args.only == "forward":
                 step.forward_only("default")
+            elif args.only == "metric":
+                step.metric()
             else:
                 step.gradients_only()
         torch.cuda.synchronize()
@@ -406,6 +426,23 @@ def main():
         torch.cuda.synchronize()
         result["breakdown"]["forward_ms_fp32_matrix_cores"] = round(a.elapsed_time(b) / args.steps, 4)
         result["config"]["forward_math"] = "fp32 operands as three bf16 matrix-core products, fp32 accumulation"
+    # side measurement: the reduce metric over the flat parameter vector
+    step.metric_setup()
+    for _ in range(2):
+        step.metric()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        step.metric()
+    b.record()
+    torch.cuda.synchronize()
+    m_ms = a.elapsed_time(b) / args.steps
+    m_units = wl.pop * step.center.numel()
+    result["breakdown"]["reduce_metric"] = {
+        "n_params": step.center.numel(), "ms": round(m_ms, 4),
+        "elements_per_s": m_units / (m_ms * 1e-3),
+        "frac_of_hash_peak": round(m_units / (m_ms * 1e-3) / HASH_PEAK_PER_S, 4),
+    }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
     print(json.dumps(result), flush=True)

@@ -147,12 +147,39 @@ def test_binding_checks_pop_size():
         vn.virtual_weight_gradient(torch.ones(4, device=dev), s, (2, 3), 0.0, 4, 0)
 
 
-@pytest.mark.parametrize("pop,n,offset", [(6, 1000, 0), (3, 269322, 5), (1, 1, 2**35), (40, 4097, 77)])
+@pytest.mark.parametrize("pop,n,offset", [(6, 1000, 0), (3, 269322, 5), (1, 1, 2**35), (40, 4097, 77), (2, 3, 9),
+                                          (5, 4096 * 3 + 2, 1), (300, 2051, 13), (1, (1 << 20) + 3, 3),
+                                          (200, 140000, 0)])
 def test_reduce_metric(pop, n, offset):
+    print(f"reduce metric pop={pop} n={n}", flush=True)
     rng = np.random.default_rng(n)
     center = rng.standard_normal(n).astype(np.float32)
     seeds = np.arange(pop, dtype=np.int64) * 31 - 7
     sig = 0.3
     got = vn.virtual_reduce_metric(to_dev(center), to_dev(seeds), sig, n, offset).cpu().numpy()
     ref = oracle.reduce_metric(center, seeds, sigma32(sig), n, offset)
+    assert_close(got, ref, TOL_F32, "reduce metric")
+
+
+def test_reduce_metric_repeat_bit_identical():
+    """Segmented (small population, long vector): partial sums in a fixed order."""
+    pop, n = 3, 600001
+    center = to_dev(np.random.default_rng(1).standard_normal(n).astype(np.float32))
+    seeds = to_dev(np.array([4, 5, 6], dtype=np.int64))
+    a = vn.virtual_reduce_metric(center, seeds, 0.1, n, 7)
+    b = vn.virtual_reduce_metric(center, seeds, 0.1, n, 7)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("sig", [0.3, 2.0 ** -101])
+def test_reduce_metric_unaligned_center_and_tiny_sigma(sig):
+    """center starting one float past a 16-byte boundary takes the scalar loads;
+    sigma below 2^-100 takes the kernel that forms sigma * N directly."""
+    pop, n, offset = 4, 300003, 21
+    rng = np.random.default_rng(5)
+    center = rng.standard_normal(n + 1).astype(np.float32)
+    seeds = np.arange(pop, dtype=np.int64) + 100
+    buf = to_dev(center)
+    got = vn.virtual_reduce_metric(buf[1:], to_dev(seeds), sig, n, offset).cpu().numpy()
+    ref = oracle.reduce_metric(center[1:], seeds, sigma32(sig), n, offset)
     assert_close(got, ref, TOL_F32, "reduce metric")

@@ -222,8 +222,20 @@ int vn_reduce_metric(const float* center, const void* seeds, int32_t seed_dtype,
   if (n_params == 0) return VN_ERR_SHAPE;  // the mean of nothing is undefined
   if (center == nullptr || seeds == nullptr || out == nullptr) return VN_ERR_NULL;
   if (!aligned(center, 4) || !aligned(out, 4) || !aligned(seeds, i32 ? 4 : 8)) return VN_ERR_ALIGN;
-  return hip_status(vn::launch_reduce_metric(center, seeds, i32, pop, n_params, sigma, offset, out,
-                                             static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // A population too small to fill the GPU with one workgroup per individual
+  // splits each individual into segments; their partial sums live in a
+  // stream-ordered temporary buffer.  Without it (allocation failed) the
+  // result is the same, computed with one workgroup per individual.
+  const int64_t ws = vn::reduce_metric_workspace_floats(pop, n_params);
+  float* work = nullptr;
+  if (ws > 0 && hipMallocAsync(reinterpret_cast<void**>(&work), static_cast<size_t>(ws) * sizeof(float), s) != hipSuccess) {
+    work = nullptr;
+    (void)hipGetLastError();
+  }
+  const hipError_t e = vn::launch_reduce_metric(center, seeds, i32, pop, n_params, sigma, offset, out, work, s);
+  if (work != nullptr) (void)hipFreeAsync(work, s);
+  return hip_status(e);
 }
 
 static int noise_common(const void* seeds, int32_t seed_dtype, int64_t pop, int64_t n, int64_t offset,

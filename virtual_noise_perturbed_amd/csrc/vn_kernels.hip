@@ -794,9 +794,18 @@ hipError_t launch_noise(const void* seeds, bool seeds_i32, int64_t pop, int64_t 
 
 // ---------------------------------------------------------------------------
 // Reduce metric: out[i] = mean_k |center[k] + sigma noise_i[offset + k]|.
-__global__ __launch_bounds__(256) void metric_kernel(const float* center, const void* seeds, bool seeds_i32,
-                                                     int64_t pop, int64_t n, float sigma, int64_t offset,
-                                                     float* out) {
+// A 1024-thread workgroup (16 waves) reduces one segment of one individual:
+// thread t takes the runs of four consecutive k starting at 4 (t + 1024 m)
+// within the segment; its sum, the wave butterfly and the sum over the 16
+// waves all have a fixed order.  With one segment per individual the
+// workgroup writes the mean; otherwise it writes a partial sum and
+// metric_finish adds an individual's partials in segment order.
+constexpr int kMetricThreads = 1024;
+
+// The same with the noise formed as N itself (for |sigma| < 2^-100).
+__global__ __launch_bounds__(256) void metric_kernel_small_sigma(const float* center, const void* seeds,
+                                                                 bool seeds_i32, int64_t pop, int64_t n, float sigma,
+                                                                 int64_t offset, float* out) {
   __shared__ float red[256];
   const int tid = threadIdx.x;
   for (int64_t i = blockIdx.x; i < pop; i += gridDim.x) {
@@ -819,10 +828,111 @@ __global__ __launch_bounds__(256) void metric_kernel(const float* center, const 
   }
 }
 
+struct MetricParams {
+  const float* center;
+  const void* seeds;
+  bool seeds_i32;
+  bool vec;           // center 16-byte aligned: runs of four as one load
+  int64_t pop, n, offset;
+  int64_t seg_len;    // elements per segment, a multiple of 4
+  int64_t n_seg;      // segments per individual
+  float sigma_q;      // sigma * 2^-24
+  float* out;         // (pop,) means when n_seg == 1, else (pop, n_seg) partial sums
+};
+
+__global__ __launch_bounds__(kMetricThreads) void metric_kernel(MetricParams p) {
+  __shared__ float red[kMetricThreads / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  constexpr uint64_t kStep = gamma_times(4 * kMetricThreads);
+  const int64_t units = p.pop * p.n_seg;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int64_t i = u / p.n_seg, seg = u - i * p.n_seg;
+    const int64_t k0 = seg * p.seg_len;
+    const int64_t k1 = k0 + p.seg_len < p.n ? k0 + p.seg_len : p.n;
+    const int64_t nvec = p.vec ? (k1 - k0) / 4 : 0;          // whole runs of four
+    const uint64_t s = load_seed(p.seeds, p.seeds_i32, i);
+    float acc = 0.0f;
+    uint64_t z = state_of(s, static_cast<uint64_t>(p.offset + k0 + 4 * tid));
+    for (int64_t v = tid; v < nvec; v += kMetricThreads) {
+      const float4 c = reinterpret_cast<const float4*>(p.center + k0)[v];
+      acc += __builtin_fabsf(__builtin_fmaf(p.sigma_q, static_cast<float>(centered_q(z)), c.x));
+      acc += __builtin_fabsf(__builtin_fmaf(p.sigma_q, static_cast<float>(centered_q(z + gamma_times(1))), c.y));
+      acc += __builtin_fabsf(__builtin_fmaf(p.sigma_q, static_cast<float>(centered_q(z + gamma_times(2))), c.z));
+      acc += __builtin_fabsf(__builtin_fmaf(p.sigma_q, static_cast<float>(centered_q(z + gamma_times(3))), c.w));
+      z += kStep;
+    }
+    for (int64_t k = k0 + 4 * nvec + tid; k < k1; k += kMetricThreads)
+      acc += __builtin_fabsf(__builtin_fmaf(
+          p.sigma_q, static_cast<float>(centered_q(state_of(s, static_cast<uint64_t>(p.offset + k)))), p.center[k]));
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, 64);
+    if (lane == 0) red[wave] = acc;
+    __syncthreads();
+    if (tid == 0) {
+      float t = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kMetricThreads / 64; ++w) t += red[w];
+      p.out[u] = p.n_seg == 1 ? t / static_cast<float>(p.n) : t;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void metric_finish(const float* partial, int64_t pop, int64_t n_seg, int64_t n,
+                                                     float* out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= pop) return;
+  float t = 0.0f;
+  for (int64_t g = 0; g < n_seg; ++g) t += partial[i * n_seg + g];
+  out[i] = t / static_cast<float>(n);
+}
+
+// Segments per individual: enough workgroups for three per CU (the most that
+// fit: 12 waves per SIMD), segments of at least 64K elements.
+static int64_t metric_segments(int64_t pop, int64_t n) {
+  constexpr int64_t kTargetGroups = 768, kMinSeg = 65536;
+  if (pop >= kTargetGroups) return 1;
+  int64_t seg = (kTargetGroups + pop - 1) / pop;
+  const int64_t by_len = n / kMinSeg;
+  if (seg > by_len) seg = by_len;
+  return seg < 1 ? 1 : seg;
+}
+
+int64_t reduce_metric_workspace_floats(int64_t pop, int64_t n) {
+  const int64_t seg = metric_segments(pop, n);
+  return seg > 1 ? pop * seg : 0;
+}
+
 hipError_t launch_reduce_metric(const float* center, const void* seeds, bool seeds_i32, int64_t pop, int64_t n,
-                                float sigma, int64_t offset, float* out, hipStream_t stream) {
-  const int64_t g = pop < 65536 ? pop : 65536;
-  metric_kernel<<<static_cast<unsigned>(g), 256, 0, stream>>>(center, seeds, seeds_i32, pop, n, sigma, offset, out);
+                                float sigma, int64_t offset, float* out, float* workspace, hipStream_t stream) {
+  // sigma * 2^-24 scales the integer noise (r >> 8) - 2^23; below 2^-100 it
+  // would be subnormal, so such a sigma takes the kernel that forms sigma * N.
+  if (sigma != 0.0f && __builtin_fabsf(sigma) < 0x1p-100f) {
+    const int64_t g = pop < 65536 ? pop : 65536;
+    metric_kernel_small_sigma<<<static_cast<unsigned>(g), 256, 0, stream>>>(center, seeds, seeds_i32, pop, n, sigma,
+                                                                            offset, out);
+    return hipGetLastError();
+  }
+  MetricParams p;
+  p.center = center;
+  p.seeds = seeds;
+  p.seeds_i32 = seeds_i32;
+  p.vec = reinterpret_cast<uintptr_t>(center) % 16 == 0;
+  p.pop = pop;
+  p.n = n;
+  p.offset = offset;
+  p.n_seg = workspace != nullptr ? metric_segments(pop, n) : 1;
+  p.seg_len = p.n_seg == 1 ? n : ((n + p.n_seg - 1) / p.n_seg + 3) / 4 * 4;
+  p.n_seg = (n + p.seg_len - 1) / p.seg_len;    // the last segment is never empty
+  p.sigma_q = sigma * 0x1p-24f;
+  p.out = p.n_seg == 1 ? out : workspace;
+  const int64_t units = pop * p.n_seg;
+  const int64_t g = units < 65536 ? units : 65536;
+  metric_kernel<<<static_cast<unsigned>(g), kMetricThreads, 0, stream>>>(p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_seg == 1) return e;
+  metric_finish<<<static_cast<unsigned>((pop + 255) / 256), 256, 0, stream>>>(workspace, pop, p.n_seg, n, out);
   return hipGetLastError();
 }
 
