@@ -35,6 +35,12 @@ CASES = [
     (2, 64, 96, 128, "bf16", True, True, 12),       # single-column-block tile, full width
     (2, 60, 72, 129, "f32", True, False, 3),        # two-block tile, second tile mostly idle
     (5, 20, 40, 3, "f32", True, False, 1),          # 32-row tile, out 3
+    # large batches: 512-row workgroups sharing one generated weight tile
+    (2, 600, 200, 300, "f32", True, False, 3),      # two row tiles, ragged column tile
+    (3, 1030, 136, 130, "bf16", True, True, 2**34), # three row tiles, shared x
+    (1, 513, 16, 128, "f32", False, False, 0),      # one k-chunk, one row past a tile
+    (2, 700, 17, 5, "f32", True, False, 8),         # in not a multiple of 4: element loads
+    (2, 300, 1000, 260, "bf16", False, True, 5),    # dead waves in the row tile
 ]
 
 

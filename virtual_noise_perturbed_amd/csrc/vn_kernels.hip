@@ -612,6 +612,258 @@ static hipError_t launch_mm_cfg(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Forward for large batches.  The 8 waves of a workgroup split 512 batch rows
+// (two 32-row blocks each) and share one 128-column tile of perturbed weights:
+// per k-chunk of KC the workgroup generates the tile once -- thread t hashes
+// the run of KC/4 consecutive k of column t / 4 -- and packs it to bf16 (hi and
+// lo planes for fp32 operands) into a double-buffered LDS tile; every wave
+// multiplies its own X rows, read straight from memory in the A layout,
+// against the whole tile.  Each noise element is generated once per 512 rows,
+// so past a few hundred rows the matrix cores, not the hash, bound the kernel.
+template <typename IN_T, bool SPLIT, int KC, bool VEC>
+__global__ __launch_bounds__(512, 1) void forward_rows_kernel(FwdParams p, int64_t n_tiles) {
+  using MF = Mfma<__bf16, 32>;
+  using Acc = typename MF::Acc;
+  constexpr int WAVES = 8;
+  constexpr int MBW = 2;                  // 32-row blocks per wave
+  constexpr int NB = 4;                   // 32-column blocks: the whole tile
+  constexpr int T = KC / 16;              // MFMA k-steps per chunk
+  constexpr int NT = NB * 32;
+  constexpr int ROWS_W = MBW * 32;
+  constexpr int ROWS = WAVES * ROWS_W;
+  constexpr int RB = NT * KC / (64 * WAVES);   // k per thread in the B tile
+  constexpr int GPC = KC / RB;                 // threads per tile column
+  constexpr int STRIDE = KC + 8;               // LDS column pitch in bf16 (16-byte pad)
+  constexpr int PLANES = SPLIT ? 2 : 1;
+  constexpr int PLANE = NT * STRIDE;
+  constexpr int BUF = PLANES * PLANE;
+  constexpr uint64_t kChunkStep = gamma_times(KC);
+  constexpr int kMfmaPerChunk = T * MBW * NB * (SPLIT ? 3 : 1);
+  constexpr int kValuPerMfma = (RB * 24 + T * MBW * 8 * (SPLIT ? 3 : 0)) / kMfmaPerChunk + 1;
+  static_assert(GPC == 4 && (RB == 4 || RB % 8 == 0), "tile generation mapping");
+
+  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 31, lh = lane >> 5;
+
+  const int64_t in = p.in, out = p.out, batch = p.batch;
+  const int64_t nfull = VEC ? in / KC : 0;     // chunks taken on the unguarded path
+  const int64_t nchunks = (in + KC - 1) / KC;
+
+  const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t i = L / n_tiles;
+  const int64_t tile = L - i * n_tiles;
+  const uint64_t s = load_seed(p.seeds, p.seeds_i32, i);
+  const IN_T* __restrict__ xi = static_cast<const IN_T*>(p.x) + i * p.x_pop_stride;
+  const IN_T* __restrict__ w = static_cast<const IN_T*>(p.w);
+  const int64_t j0 = tile * NT;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * ROWS + wave * ROWS_W;
+  // A wave whose rows all lie past the batch only helps build the tiles.
+  const bool live = m0 < batch;
+
+  // ---- tile generation: this thread's column and run of RB k.  Columns past
+  // `out` read the last column: they only feed discarded outputs.
+  const int gcol = tid / GPC;
+  const int gk = (tid % GPC) * RB;
+  int64_t gj = j0 + gcol;
+  gj = gj < out ? gj : out - 1;
+  const IN_T* wsrc = w + gj * in + gk;
+  uint64_t z = state_of(s, static_cast<uint64_t>(p.offset + gj * in + gk));
+  const int gdst = gcol * STRIDE + gk;
+
+  // ---- A side: row ln of each of the wave's row blocks, k-group lh.  Rows
+  // past the batch read the last row: they only feed discarded outputs.
+  const IN_T* xrow[MBW];
+#pragma unroll
+  for (int mb = 0; mb < MBW; ++mb) {
+    int64_t r = m0 + mb * 32 + ln;
+    r = r < batch ? r : batch - 1;
+    xrow[mb] = xi + r * in + lh * 8;
+  }
+
+  IN_T wv[RB];                    // W run of the chunk being generated
+  IN_T xr[MBW][T][8];                     // X of the chunk being loaded
+  uint32_t ah[MBW][T][4], al[MBW][T][4];  // packed A fragments of the chunk being multiplied
+
+  auto load = [&](int64_t c, bool guarded) {
+    const int64_t k0 = c * KC;
+    if (!guarded) {
+      if constexpr (RB * sizeof(IN_T) >= 16) {
+        load_run<IN_T, RB, true>(wv, wsrc + k0);
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(wsrc + k0);
+        __builtin_memcpy(wv, &v, 8);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+        for (int t = 0; t < T; ++t) load_run<IN_T, 8, true>(xr[mb][t], xrow[mb] + k0 + t * 16);
+    } else {
+      load_run_guarded<IN_T, RB>(wv, wsrc + k0, static_cast<int>(in - k0 - gk));
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          load_run_guarded<IN_T, 8>(xr[mb][t], xrow[mb] + k0 + t * 16, static_cast<int>(in - k0 - t * 16 - lh * 8));
+    }
+  };
+  // W + sigma N of the thread's run -> LDS buffer `buf` (hi, and lo when split).
+  auto make_tile = [&](int buf) {
+    float v[RB];
+#pragma unroll
+    for (int t = 0; t < RB; ++t)
+      v[t] = __builtin_fmaf(p.sigma_q, static_cast<float>(centered_q(z + gamma_times(t))), to_f32(wv[t]));
+    z += kChunkStep;
+    uint32_t hw[RB / 2], lw[RB / 2];
+#pragma unroll
+    for (int e = 0; e < RB / 2; ++e) {
+      hw[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+      if constexpr (SPLIT) lw[e] = pack_bf16x2(v[2 * e] - bf16_lo_to_f32(hw[e]), v[2 * e + 1] - bf16_hi_to_f32(hw[e]));
+    }
+    using Packed = std::conditional_t<RB >= 8, uint4, uint2>;
+    constexpr int NPK = RB / 2 * 4 / static_cast<int>(sizeof(Packed));
+#pragma unroll
+    for (int q = 0; q < NPK; ++q) {
+      Packed h2;
+      __builtin_memcpy(&h2, &hw[q * sizeof(Packed) / 4], sizeof(Packed));
+      *reinterpret_cast<Packed*>(&lds[buf * BUF + gdst + q * sizeof(Packed) / 2]) = h2;
+      if constexpr (SPLIT) {
+        Packed l2;
+        __builtin_memcpy(&l2, &lw[q * sizeof(Packed) / 4], sizeof(Packed));
+        *reinterpret_cast<Packed*>(&lds[buf * BUF + PLANE + gdst + q * sizeof(Packed) / 2]) = l2;
+      }
+    }
+  };
+  // X of the loaded chunk -> packed A fragments (hi, and lo when split).
+  auto make_a = [&]() {
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = to_f32(xr[mb][t][2 * e]), b = to_f32(xr[mb][t][2 * e + 1]);
+          ah[mb][t][e] = pack_bf16x2(a, b);
+          if constexpr (SPLIT)
+            al[mb][t][e] = pack_bf16x2(a - bf16_lo_to_f32(ah[mb][t][e]), b - bf16_hi_to_f32(ah[mb][t][e]));
+        }
+  };
+
+  Acc acc[MBW][NB];
+#pragma unroll
+  for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = Acc{};
+
+  auto multiply = [&](int buf) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const __bf16* bsrc = &lds[buf * BUF + (nb * 32 + ln) * STRIDE + t * 16 + lh * 8];
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(bsrc);
+        bf16x8 bl;
+        if constexpr (SPLIT) bl = *reinterpret_cast<const bf16x8*>(bsrc + PLANE);
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) {
+          const bf16x8 a_h = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ah[mb][t]));
+          if constexpr (SPLIT) {
+            const bf16x8 a_l = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(al[mb][t]));
+            acc[mb][nb] = mfma_bf16<32>(a_l, bh, acc[mb][nb]);
+            acc[mb][nb] = mfma_bf16<32>(a_h, bl, acc[mb][nb]);
+          }
+          acc[mb][nb] = mfma_bf16<32>(a_h, bh, acc[mb][nb]);
+        }
+      }
+  };
+
+  // Software pipeline: iteration c loads chunk c+1, builds its tile in the
+  // other LDS buffer while the matrix cores work on chunk c, then packs the
+  // loaded X into the A fragments of chunk c+1; one barrier per iteration.
+  if (nchunks > 0) {
+    load(0, nfull == 0);
+    make_tile(0);
+    make_a();
+  }
+  __syncthreads();
+  int64_t c = 0;
+  for (; c + 1 < nfull; ++c) {
+    load(c + 1, false);
+    make_tile(static_cast<int>((c + 1) & 1));
+    if (live) {
+      multiply(static_cast<int>(c & 1));
+#pragma unroll
+      for (int k = 0; k < kMfmaPerChunk; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+      }
+    }
+    make_a();
+    __syncthreads();
+  }
+  for (; c < nchunks; ++c) {
+    const bool next = c + 1 < nchunks;
+    if (next) {
+      load(c + 1, c + 1 >= nfull);
+      make_tile(static_cast<int>((c + 1) & 1));
+    }
+    if (live) multiply(static_cast<int>(c & 1));
+    if (next) make_a();
+    __syncthreads();
+  }
+
+  // Epilogue: bias b_j + sigma nb_i[j] with nb at offset + out*in + j.
+  if (!live) return;
+  const int rb = MF::row_base(lane);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int64_t j = j0 + nb * 32 + ln;
+    if (j >= out) continue;
+    float bj = 0.0f;
+    if (p.bias != nullptr) {
+      const float nz = noise_of_state(state_of(s, static_cast<uint64_t>(p.offset + out * in + j)));
+      bj = __builtin_fmaf(p.sigma, nz, p.bias[j]);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb) {
+      const int64_t row0 = m0 + mb * 32 + rb;
+      float* __restrict__ yp = p.y + (i * batch + row0) * out + j;
+#pragma unroll
+      for (int v = 0; v < MF::NACC; ++v) {
+        const int ro = MF::row_off(v);
+        if (row0 + ro < batch) {
+          float val = acc[mb][nb][v] + bj;
+          if (p.relu) val = val > 0.0f ? val : 0.0f;
+          yp[static_cast<int64_t>(ro) * out] = val;
+        }
+      }
+    }
+  }
+}
+
+template <typename IN_T, bool SPLIT>
+static hipError_t launch_rows(const FwdParams& p, hipStream_t stream) {
+  constexpr int NT = 128, ROWS = 512;
+  const int64_t n_tiles = (p.out + NT - 1) / NT;
+  const int64_t total = p.pop * n_tiles;
+  const int64_t m_tiles = (p.batch + ROWS - 1) / ROWS;
+  if (total > kMaxGridX || m_tiles > 65535) return hipErrorInvalidConfiguration;
+  dim3 grid(static_cast<unsigned>(total), static_cast<unsigned>(m_tiles));
+  // 16-byte loads need 16-byte aligned bases, rows and individual strides.
+  const int64_t per = 16 / static_cast<int64_t>(sizeof(IN_T));
+  const bool vec = (reinterpret_cast<uintptr_t>(p.x) % 16 == 0) && (reinterpret_cast<uintptr_t>(p.w) % 16 == 0) &&
+                   (p.in % per == 0) && (p.x_pop_stride % per == 0);
+  if (vec)
+    forward_rows_kernel<IN_T, SPLIT, 32, true><<<grid, 512, 0, stream>>>(p, n_tiles);
+  else
+    forward_rows_kernel<IN_T, SPLIT, 32, false><<<grid, 512, 0, stream>>>(p, n_tiles);
+  return hipGetLastError();
+}
+
 template <typename IN_T, bool SPLIT>
 static hipError_t launch_mm_dtype(const FwdParams& p, hipStream_t stream) {
   // <DIM, MB row blocks, NB column blocks per wave, R k per lane per chunk,
@@ -623,9 +875,10 @@ static hipError_t launch_mm_dtype(const FwdParams& p, hipStream_t stream) {
   if (p.batch <= 32) return launch_mm_cfg<IN_T, SPLIT, 32, 1, 1, 16, 4>(p, stream);
   if (p.batch <= 64) return launch_mm_cfg<IN_T, SPLIT, 32, 2, 1, 16, 4>(p, stream);
   if (p.batch <= 128) return launch_mm_cfg<IN_T, SPLIT, 32, 4, 1, 16, 2>(p, stream);
-  // 256 rows per workgroup; larger batches take several row tiles (grid.y),
-  // each regenerating the same noise.
-  return launch_mm_cfg<IN_T, SPLIT, 32, 8, 1, 16, 2>(p, stream);
+  if (p.batch <= 256) return launch_mm_cfg<IN_T, SPLIT, 32, 8, 1, 16, 2>(p, stream);
+  // Larger batches: 512 rows per workgroup sharing one generated weight tile
+  // (more rows take further row tiles on grid.y).
+  return launch_rows<IN_T, SPLIT>(p, stream);
 }
 
 // WAVES: waves per SIMD the register allocation must allow.
