@@ -59,6 +59,7 @@ HASH_ISA = {              # instructions per noise element: state step, finalize
 HASH_SIMD_CYCLES = sum(n * 4.0 / PROBE_RATE[k] for k, n in HASH_ISA.items())   # per wave64 element
 HASH_PEAK_PER_S = N_SIMD * 64 * CLOCK_HZ / HASH_SIMD_CYCLES
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK = 2.5e15    # dense bf16 matrix-core FLOP/s
 
 KERNEL_SRC = os.path.join(ROOT, "virtual_noise_perturbed_amd", "csrc", "vn_kernels.hip")
 DEVICE_SRC = os.path.join(ROOT, "virtual_noise_perturbed_amd", "csrc", "vn_device.hpp")
@@ -93,7 +94,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds for the oracle baseline sample")
@@ -259,7 +260,7 @@ def cpu_baseline(wl, budget_s: float):
     t0 = time.perf_counter()
     k = 0
     while k < wl.pop and (time.perf_counter() - t0) < budget_s / 2:
-        h = wl.x[k:k + 1].astype(np.float64)
+        h = (wl.x[None] if wl.x.ndim == 2 else wl.x[k:k + 1]).astype(np.float64)
         for li, L in enumerate(wl.layers):
             h = oracle.perturbed_linear(h, L.weight, L.bias, wl.seeds[k:k + 1], sig, L.w_offset)
             if wl.relu_between and li < len(wl.layers) - 1:
@@ -363,19 +364,43 @@ def main():
             units = wl.pop * L.out_features
     achieved = units / (avg_ms[dom] * 1e-3)
     traffic = recorded_traffic(args.workload, dom)
-    roofline = {
-        "bound": "alu",
-        "kernel": dom,
-        "achieved": round(achieved / 1e9, 2),
-        "peak": round(HASH_PEAK_PER_S / 1e9, 2),
-        "unit": "G noise elements/s",
-        "frac": round(achieved / HASH_PEAK_PER_S, 4),
-        "traffic": traffic,
-        "units_per_launch": units,
-        "avg_launch_ms": round(avg_ms[dom], 4),
-        "peak_basis": (f"hash issue bound: {HASH_SIMD_CYCLES:.1f} SIMD-cycles per wave64 element "
-                       f"(ISA count x measured issue costs), {N_SIMD} SIMDs x 64 lanes x 2.4 GHz"),
-    }
+    # The binding unit of the dominant launch: the hash on the VALU, or -- for
+    # a forward with enough rows per individual -- the matrix cores.  fp32
+    # operands run as three bf16 products, so their matrix-core work is 3x.
+    mfma_work = 0.0
+    if dom.startswith("forward"):
+        L = wl.layers[int(dom[-1])]
+        mfma_work = 2.0 * wl.pop * wl.batch * L.in_features * L.out_features * (1 if wl.dtype == "bf16" else 3)
+    t_hash = units / HASH_PEAK_PER_S
+    t_mfma = mfma_work / MFMA_BF16_PEAK
+    if t_mfma > t_hash:
+        roofline = {
+            "bound": "mfma",
+            "kernel": dom,
+            "achieved": round(mfma_work / (avg_ms[dom] * 1e-3) / 1e12, 2),
+            "peak": round(MFMA_BF16_PEAK / 1e12, 1),
+            "unit": "TFLOP/s",
+            "frac": round(mfma_work / (avg_ms[dom] * 1e-3) / MFMA_BF16_PEAK, 4),
+            "traffic": traffic,
+            "flops_per_launch": mfma_work,
+            "avg_launch_ms": round(avg_ms[dom], 4),
+            "peak_basis": "dense bf16 matrix cores 2.5 PFLOP/s (fp32 operands count their three bf16 products)",
+            "hash_frac": round(achieved / HASH_PEAK_PER_S, 4),
+        }
+    else:
+        roofline = {
+            "bound": "alu",
+            "kernel": dom,
+            "achieved": round(achieved / 1e9, 2),
+            "peak": round(HASH_PEAK_PER_S / 1e9, 2),
+            "unit": "G noise elements/s",
+            "frac": round(achieved / HASH_PEAK_PER_S, 4),
+            "traffic": traffic,
+            "units_per_launch": units,
+            "avg_launch_ms": round(avg_ms[dom], 4),
+            "peak_basis": (f"hash issue bound: {HASH_SIMD_CYCLES:.1f} SIMD-cycles per wave64 element "
+                           f"(ISA count x measured issue costs), {N_SIMD} SIMDs x 64 lanes x 2.4 GHz"),
+        }
 
     value = flops_of(wl) / (ms_per_step * 1e-3) / 1e12
     result = {

@@ -45,7 +45,7 @@ def _sample_flat(rng, n_el, fin, n):
     return np.unique(idx)
 
 
-@pytest.mark.parametrize("key", [1, 2, 3, 5])
+@pytest.mark.parametrize("key", [1, 2, 3, 5, 6])
 def test_single_layer_forward(key):
     print(f"workload {key} forward", flush=True)
     wl = workloads.make(key)
@@ -58,9 +58,15 @@ def test_single_layer_forward(key):
     torch.cuda.synchronize()
     assert y.shape == (wl.pop, wl.batch, L.out_features)
     ids = list(range(wl.pop)) if wl.pop <= 8 else _pick_individuals(wl.pop)
-    ref = oracle.perturbed_linear(wl.x[ids], L.weight, L.bias, wl.seeds[ids], sig, L.w_offset)
-    got = y[ids].cpu().numpy()
-    assert_close(got, ref, tol, f"workload {key} whole individuals {ids}")
+    shared = wl.x.ndim == 2
+    # whole rows (every output column) of a few individuals; all rows unless
+    # the batch is large, then the first, middle and last rows of both row
+    # tiles they fall in
+    rows = np.arange(wl.batch) if wl.batch <= 256 else np.array([0, 1, 511, 512, wl.batch // 2, wl.batch - 1])
+    xs = wl.x[rows] if shared else wl.x[ids][:, rows]
+    ref = oracle.perturbed_linear(xs, L.weight, L.bias, wl.seeds[ids], sig, L.w_offset)
+    got = y[ids][:, torch.as_tensor(rows)].cpu().numpy()
+    assert_close(got, ref, tol, f"workload {key} whole rows of individuals {ids}")
     rng = np.random.default_rng(key)
     ii, bb, jj = _sample_outputs(rng, wl.pop, wl.batch, L.out_features, 400)
     ref_s = oracle.perturbed_linear_at(wl.x, L.weight, L.bias, wl.seeds, sig, L.w_offset, ii, bb, jj)
@@ -68,7 +74,7 @@ def test_single_layer_forward(key):
     assert_close(got_s, ref_s, tol, f"workload {key} sampled outputs")
 
 
-@pytest.mark.parametrize("key", [1, 2, 3, 5])
+@pytest.mark.parametrize("key", [1, 2, 3, 5, 6])
 def test_single_layer_gradients(key):
     print(f"workload {key} gradients", flush=True)
     wl = workloads.make(key)

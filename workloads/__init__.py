@@ -122,11 +122,12 @@ DESCRIPTIONS = {
     3: "RL policy single observation: pop 4096, batch 1, 512->256, fp32",
     4: "3-layer MLP 784->256->256->10 chained by flat offsets: pop 512, batch 64, fp32",
     5: "transformer-width projection: pop 128, batch 256, 4096->4096, bf16 operands",
+    6: "large-batch shared-input projection: pop 16, batch 4096 (one X for all), 4096->4096, bf16 operands",
 }
 
 
 def make(key: int) -> Workload:
-    """Full-size workload ``key`` (1..5)."""
+    """Full-size workload ``key`` (1..6)."""
     rng = np.random.default_rng(BASE_SEED + key)
     if key == 1:
         pop, batch, fin, fout = 8, 4, 64, 32
@@ -173,6 +174,16 @@ def make(key: int) -> Workload:
         fit = _normal(rng, (pop,))
         per, shapes = _chain([(fin, fout)], [False])
         return Workload(5, DESCRIPTIONS[5], pop, batch, "bf16", np.arange(pop, dtype=np.int64),
+                        0.001, x, [Layer(w, None, *per[0])], fit, shapes=shapes)
+    if key == 6:
+        # the large-batch regime: one (batch, in) input shared by every
+        # individual, enough rows per individual for the matrix cores to bind
+        pop, batch, fin, fout = 16, 4096, 4096, 4096
+        x = round_to_bf16(_normal(rng, (batch, fin)))
+        w = round_to_bf16(_normal(rng, (fout, fin), 1.0 / fin))
+        fit = _normal(rng, (pop,))
+        per, shapes = _chain([(fin, fout)], [False])
+        return Workload(6, DESCRIPTIONS[6], pop, batch, "bf16", np.arange(pop, dtype=np.int64),
                         0.001, x, [Layer(w, None, *per[0])], fit, shapes=shapes)
     raise ValueError(f"unknown workload {key}")
 
