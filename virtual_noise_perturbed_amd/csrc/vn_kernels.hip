@@ -654,9 +654,19 @@ __global__ __launch_bounds__(512, 1) void forward_rows_kernel(FwdParams p, int64
   const int64_t nfull = VEC ? in / KC : 0;     // chunks taken on the unguarded path
   const int64_t nchunks = (in + KC - 1) / KC;
 
+  // Work order.  With a shared X the individuals of one column tile are
+  // neighbours (they run together on one XCD and share its L2 copy of the W
+  // tile and the X rows); otherwise the column tiles of one individual are
+  // (they share that individual's X rows).
   const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t i = L / n_tiles;
-  const int64_t tile = L - i * n_tiles;
+  int64_t i, tile;
+  if (p.x_pop_stride == 0) {
+    tile = L / p.pop;
+    i = L - tile * p.pop;
+  } else {
+    i = L / n_tiles;
+    tile = L - i * n_tiles;
+  }
   const uint64_t s = load_seed(p.seeds, p.seeds_i32, i);
   const IN_T* __restrict__ xi = static_cast<const IN_T*>(p.x) + i * p.x_pop_stride;
   const IN_T* __restrict__ w = static_cast<const IN_T*>(p.w);
@@ -738,19 +748,25 @@ __global__ __launch_bounds__(512, 1) void forward_rows_kernel(FwdParams p, int64
       }
     }
   };
-  // X of the loaded chunk -> packed A fragments (hi, and lo when split).
+  // X of the loaded chunk -> packed A fragments (hi, and lo when split);
+  // bf16 operands are the fragments as loaded.
   auto make_a = [&]() {
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
-      for (int t = 0; t < T; ++t)
+      for (int t = 0; t < T; ++t) {
+        if constexpr (sizeof(IN_T) == 2) {
+          __builtin_memcpy(ah[mb][t], xr[mb][t], 16);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float a = to_f32(xr[mb][t][2 * e]), b = to_f32(xr[mb][t][2 * e + 1]);
-          ah[mb][t][e] = pack_bf16x2(a, b);
-          if constexpr (SPLIT)
-            al[mb][t][e] = pack_bf16x2(a - bf16_lo_to_f32(ah[mb][t][e]), b - bf16_hi_to_f32(ah[mb][t][e]));
+          for (int e = 0; e < 4; ++e) {
+            const float a = to_f32(xr[mb][t][2 * e]), b = to_f32(xr[mb][t][2 * e + 1]);
+            ah[mb][t][e] = pack_bf16x2(a, b);
+            if constexpr (SPLIT)
+              al[mb][t][e] = pack_bf16x2(a - bf16_lo_to_f32(ah[mb][t][e]), b - bf16_hi_to_f32(ah[mb][t][e]));
+          }
         }
+      }
   };
 
   Acc acc[MBW][NB];
