@@ -363,8 +363,6 @@ def main():
         step.run(cal)
     torch.cuda.synchronize()
     avg_ms = cal.averages()
-    fwd_ms = sum(v for k, v in avg_ms.items() if k.startswith("forward"))
-    grad_ms = sum(v for k, v in avg_ms.items() if k.startswith("grad"))
     # dominant kernel: the launch with the largest average duration
     dom = max(avg_ms, key=avg_ms.get)
 
@@ -379,6 +377,8 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     avg_ms[dom] = live.averages()[dom]
+    fwd_ms = sum(v for k, v in avg_ms.items() if k.startswith("forward"))
+    grad_ms = sum(v for k, v in avg_ms.items() if k.startswith("grad"))
     if dom == "grad_flat":
         units = wl.pop * step.flat_n
     else:

@@ -11,16 +11,21 @@
 //    multiplies) is the dominant cost of every entry point, so each noise
 //    element is generated exactly once per (individual, element) and every
 //    kernel is organised around keeping the vector ALUs busy with it.
-//  * Forward: one workgroup (4 waves) per (individual, column tile).  Each wave
-//    owns NB column blocks and ALL rows of its individual's batch, so the noise
-//    it generates for a weight element is reused by every batch row through
-//    the matrix cores.  The perturbed weights W + sigma*N are generated directly
-//    in the MFMA B-operand layout in VGPRs and never touch LDS or HBM.  The sum
-//    over k is order-free, so each lane is given a contiguous run of k for its
-//    column: consecutive noise indices differ by +GAMMA in the state (one 64-bit
-//    add per element) and the W and X loads are 16-byte vectors.  X rows are
-//    read straight from global memory in the matching A-operand layout; the 4
-//    waves of a workgroup read the same rows, which the L1/L2 caches serve.
+//  * Forward (forward_mm_kernel, up to 256 rows): one workgroup (4 or 8 waves)
+//    per (individual, column tile).  Each wave owns NB column blocks and ALL
+//    rows of its individual's batch, so the noise it generates for a weight
+//    element is reused by every batch row through the matrix cores.  The
+//    perturbed weights W + sigma*N are generated directly in the MFMA
+//    B-operand layout in VGPRs and never touch LDS or HBM.  The sum over k is
+//    order-free, so each lane is given a contiguous run of k for its column:
+//    consecutive noise indices differ by +GAMMA in the state (one 64-bit add
+//    per element) and the W loads are 16-byte vectors.  The X rows of a
+//    k-chunk are staged once per workgroup in LDS and read by every wave.
+//  * Forward, larger batches (forward_rows_kernel): the waves split 512 rows
+//    and share one LDS tile of W + sigma*N per k-chunk, so the noise is
+//    generated once per 512 rows.
+//  * Forward, fp32 matrix cores (forward_kernel): the same ownership with X
+//    read straight from memory in the A layout; exact fp32 products.
 //  * Gradients: element-major (lanes own consecutive elements, the population is
 //    walked with wave-uniform scalar loads of seed and fitness, split over the 4
 //    waves and reduced through LDS in a fixed order) for large blocks;
@@ -285,7 +290,7 @@ __global__ __launch_bounds__(256, WAVES) void forward_kernel(FwdParams p, int64_
 //     which leaves a relative error of about 2^-16 per product (the dropped
 //     lo*lo term and the split residuals); the sum is accumulated in fp32.
 // The X rows of a k-chunk are loaded once per workgroup (not once per wave),
-// split if needed, and kept in a double-buffered LDS tile that all 4 waves
+// split if needed, and kept in a double-buffered LDS tile that all the waves
 // read; one barrier per chunk.  The noise side is as in forward_kernel:
 // each lane generates its column's run of R = 16 consecutive k in registers.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -300,8 +305,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
 
-template <typename IN_T, bool SPLIT, int DIM, int MB, int NB, int R, int WAVES, bool VEC>
-__global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int64_t n_tiles) {
+template <typename IN_T, bool SPLIT, int DIM, int MB, int NB, int R, int WAVES, int WPG, bool VEC>
+__global__ __launch_bounds__(64 * WPG, WAVES) void forward_mm_kernel(FwdParams p, int64_t n_tiles) {
   using MF = Mfma<__bf16, DIM>;
   using Acc = typename MF::Acc;
   constexpr int H = MF::H;            // k-slot groups per MFMA
@@ -309,18 +314,19 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
   constexpr int T = R / 8;            // MFMAs per (row block, column block) per chunk
   constexpr int KC = H * R;           // k per chunk
   constexpr int ROWS = MB * DIM;
-  constexpr int NT = 4 * NB * DIM;
+  constexpr int NT = WPG * NB * DIM;
+  constexpr int NTHR = 64 * WPG;
   constexpr int STRIDE = KC + 8;      // LDS row pitch in bf16 (16-byte pad against bank conflicts)
   constexpr int PLANES = SPLIT ? 2 : 1;
   constexpr int PLANE = ROWS * STRIDE;
   constexpr int BUF = PLANES * PLANE;
   // A segment is SEGK consecutive k of one X row: 8, or 4 for fp32 when the
-  // tile has fewer than 256 eight-wide segments (so no thread repeats one).
-  constexpr int SEGK = (sizeof(IN_T) == 4 && ROWS * KC / 8 < 256) ? 4 : 8;
+  // tile has fewer eight-wide segments than threads (so no thread repeats one).
+  constexpr int SEGK = (sizeof(IN_T) == 4 && ROWS * KC / 8 < NTHR) ? 4 : 8;
   constexpr int SEG_LOADS = SEGK * static_cast<int>(sizeof(IN_T)) / 16;   // 16-byte loads per segment
   constexpr int SEG_PER_ROW = KC / SEGK;
   constexpr int NSEG = ROWS * SEG_PER_ROW;
-  constexpr int SEG_PER_THREAD = (NSEG + 255) / 256;
+  constexpr int SEG_PER_THREAD = (NSEG + NTHR - 1) / NTHR;
   constexpr uint64_t kChunkStep = gamma_times(KC);
   static_assert(!SPLIT || sizeof(IN_T) == 4, "split is for fp32 operands");
   constexpr int kMfmaPerChunk = T * MB * NB * (SPLIT ? 3 : 1);
@@ -370,7 +376,7 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
     // Threads past the last segment (when the tile has fewer than 256 per
     // pass) repeat one: same source, same LDS slot, same bytes -- this keeps
     // the pipelined loop free of branches.
-    const int q = (tid + u * 256) % NSEG;
+    const int q = (tid + u * NTHR) % NSEG;
     const int row = q / SEG_PER_ROW;
     const int kk = (q % SEG_PER_ROW) * SEGK;
     int64_t b = m0 + row;
@@ -592,9 +598,11 @@ __global__ __launch_bounds__(256, WAVES) void forward_mm_kernel(FwdParams p, int
   }
 }
 
-template <typename IN_T, bool SPLIT, int DIM, int MB, int NB, int R, int WAVES>
+// WAVES: waves per SIMD the register allocation must allow; WPG: waves per
+// workgroup (each owns NB column blocks; all share the X tile).
+template <typename IN_T, bool SPLIT, int DIM, int MB, int NB, int R, int WAVES, int WPG = 4>
 static hipError_t launch_mm_cfg(const FwdParams& p, hipStream_t stream) {
-  constexpr int NT = 4 * NB * DIM;
+  constexpr int NT = WPG * NB * DIM;
   constexpr int ROWS = MB * DIM;
   const int64_t n_tiles = (p.out + NT - 1) / NT;
   const int64_t total = p.pop * n_tiles;
@@ -606,9 +614,9 @@ static hipError_t launch_mm_cfg(const FwdParams& p, hipStream_t stream) {
   const bool vec = (reinterpret_cast<uintptr_t>(p.x) % 16 == 0) && (reinterpret_cast<uintptr_t>(p.w) % 16 == 0) &&
                    (p.in % per == 0) && (p.x_pop_stride % per == 0);
   if (vec)
-    forward_mm_kernel<IN_T, SPLIT, DIM, MB, NB, R, WAVES, true><<<grid, 256, 0, stream>>>(p, n_tiles);
+    forward_mm_kernel<IN_T, SPLIT, DIM, MB, NB, R, WAVES, WPG, true><<<grid, 64 * WPG, 0, stream>>>(p, n_tiles);
   else
-    forward_mm_kernel<IN_T, SPLIT, DIM, MB, NB, R, WAVES, false><<<grid, 256, 0, stream>>>(p, n_tiles);
+    forward_mm_kernel<IN_T, SPLIT, DIM, MB, NB, R, WAVES, WPG, false><<<grid, 64 * WPG, 0, stream>>>(p, n_tiles);
   return hipGetLastError();
 }
 
@@ -889,7 +897,10 @@ static hipError_t launch_mm_dtype(const FwdParams& p, hipStream_t stream) {
   // columns past `out` (whole waves past it are skipped in the kernel).
   if (p.out <= 16 && p.batch <= 64) return launch_mm_cfg<IN_T, SPLIT, 16, 4, 1, 16, 2>(p, stream);
   if (p.batch <= 32) return launch_mm_cfg<IN_T, SPLIT, 32, 1, 1, 16, 4>(p, stream);
-  if (p.batch <= 64) return launch_mm_cfg<IN_T, SPLIT, 32, 2, 1, 16, 4>(p, stream);
+  // 33..64 rows: 8-wave workgroups (256 columns) share each staged X tile
+  // over twice the columns, unless the layer is narrow.
+  if (p.batch <= 64 && p.out <= 128) return launch_mm_cfg<IN_T, SPLIT, 32, 2, 1, 16, 4>(p, stream);
+  if (p.batch <= 64) return launch_mm_cfg<IN_T, SPLIT, 32, 2, 1, 16, 4, 8>(p, stream);
   if (p.batch <= 128) return launch_mm_cfg<IN_T, SPLIT, 32, 4, 1, 16, 2>(p, stream);
   if (p.batch <= 256) return launch_mm_cfg<IN_T, SPLIT, 32, 8, 1, 16, 2>(p, stream);
   // Larger batches: 512 rows per workgroup sharing one generated weight tile
