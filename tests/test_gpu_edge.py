@@ -35,6 +35,13 @@ CASES = [
     (2, 64, 96, 128, "bf16", True, True, 12),       # single-column-block tile, full width
     (2, 60, 72, 129, "f32", True, False, 3),        # two-block tile, second tile mostly idle
     (5, 20, 40, 3, "f32", True, False, 1),          # 32-row tile, out 3
+    # one or two fp32 rows: the vector-ALU kernel
+    (3, 2, 100, 70, "f32", True, False, 4),         # k tail within a chunk, ragged columns
+    (2, 2, 1024, 513, "f32", False, True, 2**36),   # shared x, one column past a tile
+    (4, 1, 130, 17, "f32", True, False, 0),         # two chunks, the second partial
+    (2, 1, 6, 3, "f32", False, False, 1),           # in not a multiple of 4: element loads
+    (3, 3, 260, 140, "f32", True, False, 7),        # three rows
+    (2, 4, 64, 200, "f32", False, True, 0),         # four rows, shared x
     # large batches: 512-row workgroups sharing one generated weight tile
     (2, 600, 200, 300, "f32", True, False, 3),      # two row tiles, ragged column tile
     (3, 1030, 136, 130, "bf16", True, True, 2**34), # three row tiles, shared x

@@ -888,6 +888,125 @@ static hipError_t launch_rows(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Forward for one or two fp32 rows per individual, on the vector ALUs.  With
+// so few rows the matrix cores would idle and the bf16 split would cost more
+// than the products; here every lane multiplies in fp32 directly.  A group of
+// 16 lanes owns NCW columns in turn; lane g of the group takes the run of RL
+// consecutive k at g*RL of every chunk of 16*RL, keeps its X values for the
+// chunk in registers (reused by all NCW columns) and accumulates
+// x * (W + sigma N) per column; the 16 partial sums of a column are combined
+// by a fixed butterfly at the end.
+template <int B, int NCW, int RL, bool VEC>
+__global__ __launch_bounds__(256, 4) void forward_vec_kernel(FwdParams p, int64_t n_tiles) {
+  constexpr int KC = 16 * RL;                 // k per chunk
+  constexpr int NT = 16 * NCW;                // columns per workgroup (4 waves x 4 groups)
+  constexpr uint64_t kChunkStep = gamma_times(KC);
+  static_assert(RL % 4 == 0, "whole 16-byte loads");
+  const int tid = threadIdx.x;
+  const int grp = tid >> 4;                   // 16 groups per workgroup
+  const int g = tid & 15;
+
+  const int64_t in = p.in, out = p.out, batch = p.batch;
+  const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t i = L / n_tiles;
+  const int64_t tile = L - i * n_tiles;
+  const uint64_t s = load_seed(p.seeds, p.seeds_i32, i);
+  const float* __restrict__ xi = static_cast<const float*>(p.x) + i * p.x_pop_stride;
+  const float* __restrict__ w = static_cast<const float*>(p.w);
+
+  // this group's columns: tile*NT + grp + 16*c, c < NCW (clamped past `out`)
+  const float* wrow[NCW];
+  uint64_t z[NCW];
+#pragma unroll
+  for (int c = 0; c < NCW; ++c) {
+    int64_t j = tile * NT + grp + 16 * c;
+    j = j < out ? j : out - 1;
+    wrow[c] = w + j * in + g * RL;
+    z[c] = state_of(s, static_cast<uint64_t>(p.offset + j * in + g * RL));
+  }
+  float acc[NCW][B];
+#pragma unroll
+  for (int c = 0; c < NCW; ++c)
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[c][b] = 0.0f;
+
+  const int64_t nchunks = (in + KC - 1) / KC;
+  const int64_t nfull = VEC ? in / KC : 0;
+  for (int64_t ch = 0; ch < nchunks; ++ch) {
+    const int64_t k0 = ch * KC + g * RL;
+    const bool whole = ch < nfull;
+    const int valid = whole ? RL : static_cast<int>(in - k0);
+    float xv[B][RL];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int64_t bb = b < batch ? b : batch - 1;   // rows past the batch only feed discarded outputs
+      const float* xs = xi + bb * in + k0;
+      if (whole)
+        load_run<float, RL, true>(xv[b], xs);
+      else
+        load_run_guarded<float, RL>(xv[b], xs, valid);
+    }
+#pragma unroll
+    for (int c = 0; c < NCW; ++c) {
+      float wv[RL];
+      if (whole)
+        load_run<float, RL, true>(wv, wrow[c] + ch * KC);
+      else
+        load_run_guarded<float, RL>(wv, wrow[c] + ch * KC, valid);
+#pragma unroll
+      for (int t = 0; t < RL; ++t) {
+        const float wp = __builtin_fmaf(p.sigma_q, static_cast<float>(centered_q(z[c] + gamma_times(t))), wv[t]);
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[c][b] = __builtin_fmaf(xv[b][t], wp, acc[c][b]);
+      }
+      z[c] += kChunkStep;
+    }
+  }
+
+  // Combine the 16 partial sums of each column (fixed butterfly), epilogue.
+#pragma unroll
+  for (int c = 0; c < NCW; ++c) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      float v = acc[c][b];
+#pragma unroll
+      for (int d = 8; d >= 1; d >>= 1) v += __shfl_xor(v, d, 16);
+      acc[c][b] = v;
+    }
+    const int64_t j = tile * NT + grp + 16 * c;
+    if (g != 0 || j >= out) continue;
+    float bj = 0.0f;
+    if (p.bias != nullptr) {
+      const float nz = noise_of_state(state_of(s, static_cast<uint64_t>(p.offset + out * in + j)));
+      bj = __builtin_fmaf(p.sigma, nz, p.bias[j]);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      if (b >= batch) break;
+      float val = acc[c][b] + bj;
+      if (p.relu) val = val > 0.0f ? val : 0.0f;
+      p.y[(i * batch + b) * out + j] = val;
+    }
+  }
+}
+
+template <int B>
+static hipError_t launch_vec(const FwdParams& p, hipStream_t stream) {
+  constexpr int NCW = B >= 4 ? 2 : 4, RL = 8;   // columns per lane group, k per lane per chunk
+  constexpr int NT = 16 * NCW;
+  const int64_t n_tiles = (p.out + NT - 1) / NT;
+  const int64_t total = p.pop * n_tiles;
+  if (total > kMaxGridX) return hipErrorInvalidConfiguration;
+  const bool vec = (reinterpret_cast<uintptr_t>(p.x) % 16 == 0) && (reinterpret_cast<uintptr_t>(p.w) % 16 == 0) &&
+                   (p.in % 4 == 0) && (p.x_pop_stride % 4 == 0);
+  if (vec)
+    forward_vec_kernel<B, NCW, RL, true><<<static_cast<unsigned>(total), 256, 0, stream>>>(p, n_tiles);
+  else
+    forward_vec_kernel<B, NCW, RL, false><<<static_cast<unsigned>(total), 256, 0, stream>>>(p, n_tiles);
+  return hipGetLastError();
+}
+
 template <typename IN_T, bool SPLIT>
 static hipError_t launch_mm_dtype(const FwdParams& p, hipStream_t stream) {
   // <DIM, MB row blocks, NB column blocks per wave, R k per lane per chunk,
@@ -945,6 +1064,13 @@ static hipError_t launch_fwd_dtype(const FwdParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_forward_f32(const FwdParams& p, hipStream_t stream) {
+  switch (p.batch) {
+    case 1: return launch_vec<1>(p, stream);
+    case 2: return launch_vec<2>(p, stream);
+    case 3: return launch_vec<3>(p, stream);
+    case 4: return launch_vec<4>(p, stream);
+    default: break;
+  }
   return launch_mm_dtype<float, true>(p, stream);
 }
 hipError_t launch_forward_f32_exact(const FwdParams& p, hipStream_t stream) {
