@@ -25,7 +25,8 @@
  *
  * Conventions for every entry point below:
  *  - All pointers except those of vn_compute_offsets are DEVICE pointers owned
- *    by the caller.  The library allocates no memory and keeps no state.
+ *    by the caller.  The library keeps no state; the only memory it takes is
+ *    the small stream-ordered temporary buffer of vn_reduce_metric (see there).
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = null stream).
  *    VN_OK means "validated and enqueued"; outputs are valid once the stream
  *    reaches the launch.  Arguments are validated before any HIP call and a
