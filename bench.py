@@ -100,6 +100,8 @@ def parse():
                     help="approximate CPU seconds for the oracle baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (to scale memory counters)")
+    ap.add_argument("--fused-chain", action="store_true",
+                    help="run a multi-layer workload's forward through the fused chain entry point")
     ap.add_argument("--only", choices=["forward", "gradient", "metric"], default=None,
                     help="run only one kernel family in the timed steps (for profiling runs)")
     return ap.parse_args()
@@ -108,7 +110,7 @@ def parse():
 class Step:
     """The workload's tensors on the device and one pass of the hot path."""
 
-    def __init__(self, wl, torch, vn, device):
+    def __init__(self, wl, torch, vn, device, fused=False):
         self.wl = wl
         self.vn = vn
         self.torch = torch
@@ -124,6 +126,11 @@ class Step:
         # outputs preallocated so the step does no allocation
         self.ys = [torch.empty((wl.pop, wl.batch, L.out_features), dtype=torch.float32, device=device)
                    for L in wl.layers]
+        # --fused-chain: all layers in one vn_perturbed_mlp launch (outputs at
+        # most 256 wide, batch at most 64).  Off by default: at the 3-layer
+        # MLP's shape one launch per layer is as fast or faster.
+        fits = all(L.out_features <= 256 for L in wl.layers) and wl.batch <= 64
+        self.chain_from = 0 if (fused and len(wl.layers) > 1 and fits) else None
         # Gradient blocks.  When the parameter blocks tile one flat range of
         # noise offsets (weights then bias of each layer, layer after layer),
         # the whole gradient is one launch over that range and each block is a
@@ -145,16 +152,34 @@ class Step:
         self.gws = [view(L.w_offset, L.out_features * L.in_features) for L in wl.layers]
         self.gbs = [None if L.bias is None else view(L.b_offset, L.out_features) for L in wl.layers]
 
+    def forward_launches(self, math="default"):
+        """(name, fn) for each forward launch of the step: one per layer, or
+        one fused chain ("forward_chain") under --fused-chain; math mode "f32"
+        keeps one launch per layer."""
+        wl, vn = self.wl, self.vn
+        n = len(self.layers)
+        out = []
+        h = self.x
+        chain_from = self.chain_from if math == "default" else None
+        for li, (L, w, b) in enumerate(self.layers):
+            if chain_from is not None and li == chain_from:
+                rest = self.layers[li:]
+                out.append(("forward_chain", lambda h=h, rest=rest: vn.virtual_perturbed_mlp(
+                    h, [w_ for _, w_, _ in rest], [b_ for _, _, b_ in rest], self.seeds, wl.sigma,
+                    [L_.w_offset for L_, _, _ in rest], activation="relu" if wl.relu_between else None,
+                    out=self.ys[-1])))
+                break
+            act = "relu" if (wl.relu_between and li < n - 1) else None
+            y = self.ys[li]
+            out.append((f"forward{li}", lambda h=h, w=w, b=b, L=L, y=y, act=act: vn.virtual_perturbed_linear(
+                h, w, b, self.seeds, wl.sigma, L.w_offset, activation=act, out=y, math=math)))
+            h = y
+        return out
+
     def forward_only(self, math):
         """Forward of every layer in the given math mode (for a side measurement)."""
-        wl, vn = self.wl, self.vn
-        h = self.x
-        n = len(self.layers)
-        for li, (L, w, b) in enumerate(self.layers):
-            act = "relu" if (wl.relu_between and li < n - 1) else None
-            vn.virtual_perturbed_linear(h, w, b, self.seeds, wl.sigma, L.w_offset, activation=act,
-                                        out=self.ys[li], math=math)
-            h = self.ys[li]
+        for _, fn in self.forward_launches(math):
+            fn()
 
     def metric_setup(self):
         """The flat parameter vector (weights then bias of each layer) as the
@@ -205,14 +230,8 @@ class Step:
             fn()
             b.record()
 
-        h = self.x
-        n = len(self.layers)
-        for li, (L, w, b) in enumerate(self.layers):
-            act = "relu" if (wl.relu_between and li < n - 1) else None
-            y = self.ys[li]
-            timed(f"forward{li}", lambda h=h, w=w, b=b, L=L, y=y, act=act: vn.virtual_perturbed_linear(
-                h, w, b, self.seeds, wl.sigma, L.w_offset, activation=act, out=y))
-            h = y
+        for name, fn in self.forward_launches():
+            timed(name, fn)
         for name, fn in self.gradient_launches():
             timed(name, fn)
 
@@ -334,7 +353,7 @@ def main():
         copy_calibration(torch, device)
         return
     wl = workloads.make(args.workload)
-    step = Step(wl, torch, vn, device)
+    step = Step(wl, torch, vn, device, fused=args.fused_chain)
     if args.only is not None:
         # profiling aid: the timed steps of one kernel family only
         if args.only == "metric":
@@ -357,7 +376,7 @@ def main():
     # Per-launch durations of every kernel family, from event-bracketed steps
     # outside the timed region (an event pair on the stream costs the GPU
     # several microseconds, which would inflate the step time).
-    n_launch = len(step.layers) + len(step.gradient_launches())
+    n_launch = len(step.forward_launches()) + len(step.gradient_launches())
     cal = EventLog(torch, n_launch * max(args.steps // 5, 4))
     for _ in range(max(args.steps // 5, 4)):
         step.run(cal)
@@ -379,8 +398,12 @@ def main():
     avg_ms[dom] = live.averages()[dom]
     fwd_ms = sum(v for k, v in avg_ms.items() if k.startswith("forward"))
     grad_ms = sum(v for k, v in avg_ms.items() if k.startswith("grad"))
+    chain_layers = wl.layers[step.chain_from:] if step.chain_from is not None else []
     if dom == "grad_flat":
         units = wl.pop * step.flat_n
+    elif dom == "forward_chain":
+        units = wl.pop * sum(L.out_features * L.in_features + (L.out_features if L.bias is not None else 0)
+                             for L in chain_layers)
     else:
         L = wl.layers[int(dom[-1])]
         if dom.startswith("forward"):
@@ -396,8 +419,9 @@ def main():
     # operands run as three bf16 products, so their matrix-core work is 3x.
     mfma_work = 0.0
     if dom.startswith("forward"):
-        L = wl.layers[int(dom[-1])]
-        mfma_work = 2.0 * wl.pop * wl.batch * L.in_features * L.out_features * (1 if wl.dtype == "bf16" else 3)
+        Ls = chain_layers if dom == "forward_chain" else [wl.layers[int(dom[-1])]]
+        mfma_work = sum(2.0 * wl.pop * wl.batch * L.in_features * L.out_features for L in Ls) * \
+            (1 if wl.dtype == "bf16" else 3)
     t_hash = units / HASH_PEAK_PER_S
     t_mfma = mfma_work / MFMA_BF16_PEAK
     if t_mfma > t_hash:

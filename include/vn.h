@@ -139,6 +139,44 @@ int vn_perturbed_linear(const void* x, int64_t x_pop_stride, const void* w, int3
                         float* y, void* stream);
 
 /*
+ * A chain of perturbed layers in one call: the model equation applied
+ * layer after layer as an MLP evaluates it (API entry virtual_perturbed_linear
+ * per layer, the parameter blocks chained as in compute_offsets):
+ *   h_0 = x_i,   h_{l+1} = act(h_l (W_l + sigma N_i^(l))^T + (b_l + sigma nb_i^(l)))
+ *   y[i] = h_{n_layers}   (act is applied between layers, not after the last)
+ * Layer l's weight noise is at offsets[l] + j*in_l + k and its bias noise at
+ * offsets[l] + out_l*in_l + j: each layer is vn_perturbed_linear with that
+ * offset, and the call equals n_layers such calls with fp32 activations
+ * passed between them, except that the intermediate activations never leave
+ * the GPU's on-chip memory and the chain is one launch.
+ *   n_layers   1..8
+ *   dims       HOST, n_layers + 1 widths (in_0, out_0 = in_1, ...): in_0 >= 1,
+ *              every output width 1..256
+ *   weights    HOST array of n_layers DEVICE pointers: (dims[l+1], dims[l]) in `dtype`
+ *   biases     HOST array of n_layers DEVICE pointers to fp32 (dims[l+1],) or NULL
+ *              entries (no bias term and no bias noise); NULL = no biases at all
+ *   offsets    HOST, n_layers weight-block noise offsets (>= 0)
+ *   x          (batch, dims[0]) rows of individual i at x + i*x_pop_stride
+ *              elements (x_pop_stride = batch*dims[0], or 0 for a shared input)
+ *   batch      0..64
+ *   activation VN_ACT_NONE or VN_ACT_RELU, between layers
+ *   y          (pop, batch, dims[n_layers]) fp32
+ * Precision as vn_perturbed_linear's default math for more than 4 rows (fp32
+ * operands as three bf16 products); for VN_BF16 the
+ * intermediate activations are rounded to bf16 (nearest even), as a caller
+ * feeding the next bf16 layer would.  Errors: VN_ERR_SHAPE for an output
+ * width outside 1..256, in_0 < 1, batch > 64 or n_layers outside 1..8;
+ * VN_ERR_OVERFLOW when batch*in_0 or a layer's last noise index overflows
+ * int64; VN_ERR_VALUE also for
+ * 0 < |sigma| < 2^-100 (take such layers through vn_perturbed_linear).
+ */
+int vn_perturbed_mlp(const void* x, int64_t x_pop_stride, int32_t dtype, int32_t n_layers,
+                     const int64_t* dims, const void* const* weights, const float* const* biases,
+                     const int64_t* offsets, const void* seeds, int32_t seed_dtype, int64_t pop,
+                     int64_t batch, float sigma, int32_t activation, float* y, void* stream);
+
+
+/*
  * Weight gradient (API entry virtual_weight_gradient):
  *   grad_w[j,k] = sum_i fitness[i] N_i[j,k] / (pop_size sigma),  N_i at offset + j*in + k
  *   fitness  (pop_size,) fp32;  seeds (pop_size,) int64 or int32

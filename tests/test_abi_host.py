@@ -172,6 +172,54 @@ def test_metric_and_noise_validation(lib):
     assert lib.vn_noise_f32(FAKE, 0, 2, 4, 2**63 - 1, FAKE, None) == E.VN_ERR_OVERFLOW
 
 
+def mlp(lib, **kw):
+    a = dict(x=FAKE, stride=0, dtype=_lib.VN_F32, dims=[8, 6, 4], w=[FAKE, FAKE], b=None, offsets=[0, 100],
+             seeds=FAKE, sdt=_lib.VN_I64, pop=3, batch=5, sigma=0.1, act=_lib.VN_ACT_RELU, y=FAKE)
+    a.update(kw)
+    n = kw.get("n", 2)
+    dims = None if a["dims"] is None else (ctypes.c_int64 * len(a["dims"]))(*a["dims"])
+    w = None if a["w"] is None else (ctypes.c_void_p * len(a["w"]))(*[None if p is None else p.value for p in a["w"]])
+    b = None if a["b"] is None else (ctypes.c_void_p * len(a["b"]))(*[None if p is None else p.value for p in a["b"]])
+    offs = None if a["offsets"] is None else (ctypes.c_int64 * len(a["offsets"]))(*a["offsets"])
+    return lib.vn_perturbed_mlp(a["x"], a["stride"], a["dtype"], n, dims, w, b, offs, a["seeds"], a["sdt"],
+                                a["pop"], a["batch"], a["sigma"], a["act"], a["y"], None)
+
+
+def test_mlp_validation(lib):
+    """Every call fails validation or has a zero extent: nothing is launched."""
+    E = _lib
+    assert mlp(lib, dtype=9) == E.VN_ERR_DTYPE
+    assert mlp(lib, sdt=9) == E.VN_ERR_DTYPE
+    assert mlp(lib, n=0) == E.VN_ERR_SHAPE
+    assert mlp(lib, n=9, dims=[4] * 10, w=[FAKE] * 9, offsets=[0] * 9) == E.VN_ERR_SHAPE
+    assert mlp(lib, dims=[8, 257, 4]) == E.VN_ERR_SHAPE          # output widths are at most 256
+    assert mlp(lib, dims=[8, 4, 257]) == E.VN_ERR_SHAPE
+    assert mlp(lib, dims=[0, 4, 4]) == E.VN_ERR_SHAPE
+    assert mlp(lib, dims=[2**62, 4, 4]) == E.VN_ERR_OVERFLOW     # batch * dims[0] overflows
+    assert mlp(lib, dims=[8, 0, 4]) == E.VN_ERR_SHAPE
+    assert mlp(lib, batch=65) == E.VN_ERR_SHAPE                  # batches are at most 64
+    assert mlp(lib, pop=-1) == E.VN_ERR_SHAPE
+    assert mlp(lib, stride=7) == E.VN_ERR_SHAPE                  # neither 0 nor batch*dims[0]
+    assert mlp(lib, dims=None) == E.VN_ERR_NULL
+    assert mlp(lib, w=None) == E.VN_ERR_NULL
+    assert mlp(lib, offsets=None) == E.VN_ERR_NULL
+    assert mlp(lib, sigma=float("nan")) == E.VN_ERR_VALUE
+    assert mlp(lib, sigma=2.0 ** -110) == E.VN_ERR_VALUE         # sigma * 2^-24 would be subnormal
+    assert mlp(lib, act=4) == E.VN_ERR_VALUE
+    assert mlp(lib, offsets=[0, -1]) == E.VN_ERR_VALUE
+    assert mlp(lib, offsets=[0, 2**63 - 10]) == E.VN_ERR_OVERFLOW
+    assert mlp(lib, x=NULL) == E.VN_ERR_NULL
+    assert mlp(lib, y=NULL) == E.VN_ERR_NULL
+    assert mlp(lib, seeds=NULL) == E.VN_ERR_NULL
+    assert mlp(lib, w=[FAKE, None]) == E.VN_ERR_NULL
+    assert mlp(lib, w=[FAKE, ctypes.c_void_p(0x10002)]) == E.VN_ERR_ALIGN
+    assert mlp(lib, b=[FAKE, ctypes.c_void_p(0x10002)]) == E.VN_ERR_ALIGN
+    assert mlp(lib, y=ctypes.c_void_p(0x10002)) == E.VN_ERR_ALIGN
+    assert mlp(lib, x=ctypes.c_void_p(0x10002)) == E.VN_ERR_ALIGN
+    assert mlp(lib, pop=0, x=NULL, y=NULL, seeds=NULL) == E.VN_OK
+    assert mlp(lib, batch=0, y=NULL) == E.VN_OK
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(2, 3)

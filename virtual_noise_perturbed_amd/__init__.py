@@ -23,6 +23,7 @@ from ._lib import VNError, VN_ACT_NONE, VN_ACT_RELU  # noqa: F401
 __all__ = [
     "compute_offsets",
     "virtual_perturbed_linear",
+    "virtual_perturbed_mlp",
     "virtual_weight_gradient",
     "virtual_bias_gradient",
     "virtual_flat_gradient",
@@ -156,6 +157,83 @@ def virtual_perturbed_linear(x: torch.Tensor, weight: torch.Tensor, bias: Option
                                  pop, batch, in_f, out_f, float(sigma), int(offset), act, mm,
                                  _ptr(y), _stream(dev))
     _lib.check("vn_perturbed_linear", st)
+    return y
+
+
+def virtual_perturbed_mlp(x: torch.Tensor, weights: Sequence[torch.Tensor],
+                          biases: Optional[Sequence[Optional[torch.Tensor]]], seeds: torch.Tensor,
+                          sigma: float, offsets: Sequence[int], activation: Optional[str] = "relu",
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """A chain of narrow perturbed layers in one launch: ``virtual_perturbed_linear``
+    applied layer after layer (layer ``l`` with noise offset ``offsets[l]``), the
+    activation between layers, the intermediate activations kept on chip.
+
+    x: (batch, in0) shared or (pop, batch, in0); weights[l]: (out_l, in_l) in x's
+    dtype with every width in 1..256; biases: None or a list of (out_l,) tensors /
+    None; batch <= 64.  Returns (pop, batch, out_last) float32.
+    """
+    lib = _lib.load()
+    n = len(weights)
+    if n < 1:
+        raise ValueError("at least one layer")
+    dev = weights[0].device
+    for t in weights:
+        _require_device("weights", t, dev)
+    _require_device("x", x, dev)
+    dtype = weights[0].dtype
+    if any(t.dtype != dtype for t in weights) or x.dtype != dtype:
+        raise TypeError("x and every weight must share one dtype")
+    dt = {torch.float32: _lib.VN_F32, torch.bfloat16: _lib.VN_BF16}.get(dtype)
+    if dt is None:
+        raise TypeError(f"unsupported dtype {dtype} (float32 or bfloat16)")
+    s, kind = _seeds(seeds, dev)
+    pop = s.shape[0]
+    dims = [int(weights[0].shape[1])] + [int(t.shape[0]) for t in weights]
+    for l, t in enumerate(weights):
+        if t.dim() != 2 or int(t.shape[1]) != dims[l]:
+            raise ValueError(f"weights[{l}] must be (out, {dims[l]})")
+    if len(offsets) != n:
+        raise ValueError("one offset per layer")
+    if x.dim() == 2:
+        batch, stride = x.shape[0], 0
+    elif x.dim() == 3:
+        if x.shape[0] != pop:
+            raise ValueError(f"x has {x.shape[0]} individuals, seeds has {pop}")
+        batch, stride = x.shape[1], x.shape[1] * dims[0]
+    else:
+        raise ValueError("x must be (batch, in) or (pop, batch, in)")
+    if x.shape[-1] != dims[0]:
+        raise ValueError("x and weights[0] disagree on in_features")
+    bs = [None] * n if biases is None else list(biases)
+    if len(bs) != n:
+        raise ValueError("one bias (or None) per layer")
+    bc = []
+    for l, b in enumerate(bs):
+        if b is None:
+            bc.append(None)
+            continue
+        _require_device("bias", b, dev)
+        if b.shape != (dims[l + 1],):
+            raise ValueError(f"biases[{l}] must be ({dims[l + 1]},)")
+        bc.append(b.to(torch.float32).contiguous())
+    act = {None: _lib.VN_ACT_NONE, "none": _lib.VN_ACT_NONE, "relu": _lib.VN_ACT_RELU}.get(activation)
+    if act is None:
+        raise ValueError(f"unknown activation {activation!r}")
+    wc = [t.contiguous() for t in weights]
+    xc = x.contiguous()
+    if out is None:
+        y = torch.empty((pop, batch, dims[-1]), dtype=torch.float32, device=dev)
+    else:
+        if out.shape != (pop, batch, dims[-1]) or out.dtype != torch.float32 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float32 (pop, batch, out_last) tensor")
+        y = out
+    dims_arr = (ctypes.c_int64 * (n + 1))(*dims)
+    w_arr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in wc])
+    b_arr = (ctypes.c_void_p * n)(*[0 if b is None else b.data_ptr() for b in bc])
+    o_arr = (ctypes.c_int64 * n)(*[int(o) for o in offsets])
+    st = lib.vn_perturbed_mlp(_ptr(xc), stride, dt, n, dims_arr, w_arr, b_arr, o_arr, _ptr(s), kind, pop,
+                              batch, float(sigma), act, _ptr(y), _stream(dev))
+    _lib.check("vn_perturbed_mlp", st)
     return y
 
 

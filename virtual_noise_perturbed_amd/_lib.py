@@ -27,6 +27,8 @@ SIGNATURES = {
     "vn_perturbed_linear": [c_void_p, c_int64, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
                             c_int64, c_int64, c_int64, c_int64, c_float, c_int64, c_int32, c_int32,
                             c_void_p, c_void_p],
+    "vn_perturbed_mlp": [c_void_p, c_int64, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                         c_void_p, c_int32, c_int64, c_int64, c_float, c_int32, c_void_p, c_void_p],
     "vn_weight_gradient": [c_void_p, c_void_p, c_int32, c_int64, c_int64, c_int64, c_float, c_int64,
                            c_void_p, c_void_p],
     "vn_bias_gradient": [c_void_p, c_void_p, c_int32, c_int64, c_int64, c_float, c_int64,

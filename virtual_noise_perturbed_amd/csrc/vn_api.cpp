@@ -195,6 +195,71 @@ int vn_flat_gradient(const float* fitness, const void* seeds, int32_t seed_dtype
   return hip_status(vn::launch_gradient(p, static_cast<hipStream_t>(stream)));
 }
 
+int vn_perturbed_mlp(const void* x, int64_t x_pop_stride, int32_t dtype, int32_t n_layers, const int64_t* dims,
+                     const void* const* weights, const float* const* biases, const int64_t* offsets,
+                     const void* seeds, int32_t seed_dtype, int64_t pop, int64_t batch, float sigma,
+                     int32_t activation, float* y, void* stream) {
+  bool i32 = false;
+  if (dtype != VN_F32 && dtype != VN_BF16) return VN_ERR_DTYPE;
+  int st = seed_kind(seed_dtype, &i32);
+  if (st != VN_OK) return st;
+  if (n_layers < 1 || n_layers > vn::kChainMaxLayers) return VN_ERR_SHAPE;
+  if (dims == nullptr || weights == nullptr || offsets == nullptr) return VN_ERR_NULL;
+  if (pop < 0 || batch < 0 || batch > vn::kChainMaxBatch) return VN_ERR_SHAPE;
+  for (int l = 0; l <= n_layers; ++l)
+    if (dims[l] < 1 || (l > 0 && dims[l] > vn::kChainMaxWidth)) return VN_ERR_SHAPE;
+  int64_t per_x;
+  if (!mul_ok(batch, dims[0], &per_x)) return VN_ERR_OVERFLOW;
+  if (x_pop_stride != 0 && x_pop_stride != per_x) return VN_ERR_SHAPE;
+  if (!std::isfinite(sigma)) return VN_ERR_VALUE;
+  if (sigma != 0.0f && std::fabs(sigma) < 0x1p-100f) return VN_ERR_VALUE;
+  if (activation != VN_ACT_NONE && activation != VN_ACT_RELU) return VN_ERR_VALUE;
+  for (int l = 0; l < n_layers; ++l) {
+    // largest noise index of the layer: offset + out*in + out - 1
+    if (offsets[l] < 0) return VN_ERR_VALUE;
+    int64_t oi, last;
+    if (!mul_ok(dims[l + 1], dims[l], &oi) || !add_ok(oi, dims[l + 1], &oi) || !add_ok(offsets[l], oi, &last))
+      return VN_ERR_OVERFLOW;
+  }
+  int64_t ysize, xsize;
+  if (!mul_ok(pop, batch, &ysize) || !mul_ok(ysize, dims[n_layers], &ysize)) return VN_ERR_OVERFLOW;
+  if (!mul_ok(pop, x_pop_stride, &xsize)) return VN_ERR_OVERFLOW;
+  if (pop == 0 || batch == 0) return VN_OK;
+  if (pop > vn::kMaxGridX) return VN_ERR_OVERFLOW;
+  if (x == nullptr || y == nullptr || seeds == nullptr) return VN_ERR_NULL;
+  const size_t esz = dtype == VN_F32 ? 4 : 2;
+  if (!aligned(x, esz) || !aligned(y, 4) || !aligned(seeds, i32 ? 4 : 8)) return VN_ERR_ALIGN;
+
+  vn::ChainParams p;
+  p.x = x;
+  p.x_pop_stride = x_pop_stride;
+  p.n_layers = n_layers;
+  p.wvec = 0;
+  for (int l = 0; l <= n_layers; ++l) p.dims[l] = dims[l];
+  for (int l = 0; l < n_layers; ++l) {
+    if (weights[l] == nullptr) return VN_ERR_NULL;
+    if (!aligned(weights[l], esz)) return VN_ERR_ALIGN;
+    const float* b = biases != nullptr ? biases[l] : nullptr;
+    if (!aligned(b, 4)) return VN_ERR_ALIGN;
+    p.w[l] = weights[l];
+    p.bias[l] = b;
+    p.offset[l] = offsets[l];
+    if (aligned(weights[l], 16) && dims[l] % static_cast<int64_t>(16 / esz) == 0) p.wvec |= 1u << l;
+  }
+  p.relu = activation == VN_ACT_RELU;
+  // the first layer's X chunks in 16-byte loads
+  const int64_t per = static_cast<int64_t>(16 / esz);
+  p.xvec = aligned(x, 16) && dims[0] % per == 0 && x_pop_stride % per == 0;
+  p.seeds = seeds;
+  p.seeds_i32 = i32;
+  p.pop = pop;
+  p.batch = batch;
+  p.sigma = sigma;
+  p.sigma_q = sigma * 0x1p-24f;
+  p.y = y;
+  return hip_status(vn::launch_chain(p, dtype == VN_BF16, static_cast<hipStream_t>(stream)));
+}
+
 int vn_weight_gradient(const float* fitness, const void* seeds, int32_t seed_dtype, int64_t pop_size, int64_t out,
                        int64_t in, float sigma, int64_t offset, float* grad_w, void* stream) {
   if (out < 0 || in < 0) return VN_ERR_SHAPE;

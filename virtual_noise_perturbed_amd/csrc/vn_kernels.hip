@@ -1007,6 +1007,295 @@ static hipError_t launch_vec(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// A chain of layers in one launch: every output width <= 256, batch <= 64,
+// any input width.  One 8-wave workgroup per individual.  The first layer
+// streams X through a double-buffered LDS tile as forward_mm_kernel does
+// (8 waves x 32 columns, one barrier per k-chunk); its output and every
+// later activation stay in LDS (bf16 hi/lo planes for fp32 operands), so the
+// later layers need no barrier inside their k loops and no activation ever
+// reaches HBM.  In the resident layers the 32-column blocks of the output are
+// spread over the waves: with 5..8 blocks one wave per block, with fewer
+// several waves share a block and split its k-chunks (chunk c to wave
+// c mod wpb), their partial sums added through LDS in wave order.  A wave
+// hashes its columns' noise in registers exactly as forward_mm_kernel does.
+// After each layer the waves write the next activation (bias, ReLU, split)
+// over the old one; the last layer writes Y.
+template <typename IN_T, bool SPLIT>
+__global__ __launch_bounds__(512, 4) void forward_chain_kernel(ChainParams p) {
+  using MF = Mfma<__bf16, 32>;
+  using Acc = typename MF::Acc;
+  constexpr int WAVES = 8, NTHR = 64 * WAVES;
+  constexpr int MB = 2;                        // 64 rows
+  constexpr int R = 16;                        // k per lane per chunk
+  constexpr int T = R / 8;
+  constexpr int KC = MF::H * R;                // 32
+  constexpr int ROWS = MB * 32;
+  constexpr int ASTRIDE = kChainMaxWidth + 8;  // resident rows: LDS pitch in bf16 (16-byte pad)
+  constexpr int PLANES = SPLIT ? 2 : 1;
+  constexpr int PLANE = ROWS * ASTRIDE;
+  constexpr int SSTRIDE = KC + 8;              // streamed X chunks: LDS pitch
+  constexpr int SPLANE = ROWS * SSTRIDE;
+  constexpr int SBUF = PLANES * SPLANE;        // one staging buffer (two, inside `act`)
+  constexpr int SEGK = (sizeof(IN_T) == 4 && ROWS * KC / 8 < NTHR) ? 4 : 8;
+  constexpr int SEG_PER_ROW = KC / SEGK;
+  constexpr int NSEG = ROWS * SEG_PER_ROW;
+  constexpr int PART = MB * MF::NACC * 64;     // floats of one wave's partial sums
+  // all partial sums of a layer whose blocks are shared must fit the activation buffer
+  constexpr int kMaxLive = (PLANES * PLANE * 2) / (PART * 4) >= WAVES ? WAVES : (PLANES * PLANE * 2) / (PART * 4);
+  static_assert(kMaxLive >= 1, "room for one wave's partial sums");
+  static_assert(ROWS == kChainMaxBatch, "one row tile holds the batch");
+  static_assert(2 * SBUF <= PLANES * PLANE, "the staging buffers fit the activation buffer");
+  static_assert(NSEG <= NTHR, "one X segment per thread");
+
+  __shared__ __attribute__((aligned(16))) __bf16 act[PLANES * PLANE];
+  float* const part = reinterpret_cast<float*>(act);   // reused for partial sums after a layer's k loop
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 31, lh = lane >> 5;
+  // (wave-uniform values pinned to scalar registers: the k loops need every VGPR)
+  const int64_t i = __builtin_amdgcn_readfirstlane(static_cast<int>(xcd_remap(blockIdx.x, gridDim.x)));
+  const int64_t batch = p.batch;
+  const uint64_t s0 = load_seed(p.seeds, p.seeds_i32, i);
+  const uint64_t s = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(s0 >> 32))) << 32) |
+                     __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(s0));
+
+  auto put = [&](int r, int k, float v) {      // v -> act[r][k] (hi, lo)
+    const __bf16 h = static_cast<__bf16>(v);
+    act[r * ASTRIDE + k] = h;
+    if constexpr (SPLIT) act[PLANE + r * ASTRIDE + k] = static_cast<__bf16>(v - static_cast<float>(h));
+  };
+
+  for (int l = 0; l < p.n_layers; ++l) {
+    const int64_t in = p.dims[l], out = p.dims[l + 1];
+    const bool last = l + 1 == p.n_layers;
+    const bool streamed = l == 0;
+    const int nblk = static_cast<int>((out + 31) / 32);
+    int wpb = 1;                               // waves per column block (a power of two); 1 when streamed
+    if (!streamed)
+      while (wpb * 2 * nblk <= kMaxLive) wpb *= 2;
+    const int blk = wave / wpb, q = wave % wpb;
+    const bool live = blk < nblk;
+    const int64_t jbase = static_cast<int64_t>(blk) * 32;
+    Acc acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = Acc{};
+
+    int64_t jc = jbase + ln;
+    jc = jc < out ? jc : out - 1;              // columns past `out` feed only discarded outputs
+    const IN_T* __restrict__ wrow = static_cast<const IN_T*>(p.w[l]) + jc * in + lh * R;
+    uint64_t z = state_of(s, static_cast<uint64_t>(p.offset[l] + jc * in + q * KC + lh * R));
+    const uint64_t zstep = gamma_times(KC) * static_cast<uint64_t>(wpb);
+    const bool wvec = (p.wvec >> l) & 1u;
+    const int64_t nch = (in + KC - 1) / KC;
+    const int64_t nfull = wvec ? in / KC : 0;  // chunks whose lane runs all lie inside `in`
+    IN_T wv[R];
+    uint32_t bh[R / 2], bl[R / 2];
+    auto load_w = [&](int64_t c, bool guarded) {
+      if (!guarded) {
+        load_run<IN_T, R, true>(wv, wrow + c * KC);
+      } else {
+        const int64_t left = in - c * KC - lh * R;
+        load_run_guarded<IN_T, R>(wv, wrow + c * KC, left >= R ? R : static_cast<int>(left));
+      }
+    };
+    // noise of the lane's run of chunk c (as N * 2^24) folded into W + sigma N
+    auto make_b = [&](int64_t c, bool guarded) {
+      int valid = R;
+      if (guarded) {
+        const int64_t left = in - c * KC - lh * R;
+        valid = left >= R ? R : static_cast<int>(left);
+      }
+      float v[R];
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        const float w1 = __builtin_fmaf(p.sigma_q, static_cast<float>(centered_q(z + gamma_times(t))), to_f32(wv[t]));
+        v[t] = (!guarded || t < valid) ? w1 : 0.0f;
+      }
+      z += zstep;
+#pragma unroll
+      for (int e = 0; e < R / 2; ++e) {
+        bh[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+        if constexpr (SPLIT) bl[e] = pack_bf16x2(v[2 * e] - bf16_lo_to_f32(bh[e]), v[2 * e + 1] - bf16_hi_to_f32(bh[e]));
+      }
+    };
+    // MFMAs of one chunk: A fragments from `abase` (row pitch `pitch`, planes
+    // `plane` apart), B from bh/bl.
+    auto multiply = [&](const __bf16* abase, int pitch, int plane) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const bf16x8 bfh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&bh[t * 4]));
+        bf16x8 bfl;
+        if constexpr (SPLIT) bfl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&bl[t * 4]));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(abase + mb * 32 * pitch + t * 8);
+          if constexpr (SPLIT) {
+            const bf16x8 alo = *reinterpret_cast<const bf16x8*>(abase + plane + mb * 32 * pitch + t * 8);
+            acc[mb] = mfma_bf16<32>(alo, bfh, acc[mb]);
+            acc[mb] = mfma_bf16<32>(ahi, bfl, acc[mb]);
+          }
+          acc[mb] = mfma_bf16<32>(ahi, bfh, acc[mb]);
+        }
+      }
+    };
+
+    if (streamed) {
+      // ---- first layer: X chunks staged through two buffers inside `act`.
+      // Thread t stages segment t (threads past the last repeat one: same
+      // source, same slot, same bytes).  Rows past the batch read the last row.
+      const int qs = tid % NSEG;
+      const int srow = qs / SEG_PER_ROW, skk = (qs % SEG_PER_ROW) * SEGK;
+      const IN_T* __restrict__ xsrc = static_cast<const IN_T*>(p.x) + i * p.x_pop_stride +
+                                      (srow < batch ? srow : batch - 1) * in + skk;
+      const int sdst = srow * SSTRIDE + skk;
+      const int64_t xfull = p.xvec ? in / KC : 0;   // chunks staged with 16-byte loads
+      IN_T xs[SEGK];
+      auto load_x = [&](int64_t c) {
+        if (c < xfull) {
+#pragma unroll
+          for (int h = 0; h < SEGK * static_cast<int>(sizeof(IN_T)) / 16; ++h) {
+            const uint4 v = *reinterpret_cast<const uint4*>(xsrc + c * KC + h * (16 / sizeof(IN_T)));
+            __builtin_memcpy(&xs[h * (16 / sizeof(IN_T))], &v, 16);
+          }
+        } else {
+          const int64_t kmax = in - c * KC - skk;
+#pragma unroll
+          for (int e = 0; e < SEGK; ++e) xs[e] = (e < kmax) ? xsrc[c * KC + e] : static_cast<IN_T>(0.0f);
+        }
+      };
+      auto store_x = [&](int buf) {
+        using Packed = std::conditional_t<SEGK == 8, uint4, uint2>;
+        uint32_t hw[SEGK / 2], lw[SEGK / 2];
+#pragma unroll
+        for (int e = 0; e < SEGK / 2; ++e) {
+          const float a = to_f32(xs[2 * e]), b = to_f32(xs[2 * e + 1]);
+          hw[e] = pack_bf16x2(a, b);
+          if constexpr (SPLIT) lw[e] = pack_bf16x2(a - bf16_lo_to_f32(hw[e]), b - bf16_hi_to_f32(hw[e]));
+        }
+        Packed hi, lo;
+        __builtin_memcpy(&hi, hw, sizeof(Packed));
+        *reinterpret_cast<Packed*>(&act[buf * SBUF + sdst]) = hi;
+        if constexpr (SPLIT) {
+          __builtin_memcpy(&lo, lw, sizeof(Packed));
+          *reinterpret_cast<Packed*>(&act[buf * SBUF + SPLANE + sdst]) = lo;
+        }
+      };
+      auto mult_chunk = [&](int buf) { multiply(&act[buf * SBUF + ln * SSTRIDE + lh * R], SSTRIDE, SPLANE); };
+      // iteration c: stage chunk c+1, load chunk c+2, prepare B of chunk c+1
+      // while chunk c multiplies; one barrier per chunk.
+      if (nch > 0) {
+        load_x(0);
+        store_x(0);
+        if (live) {
+          load_w(0, 0 >= nfull);
+          make_b(0, 0 >= nfull);
+        }
+        if (nch > 1) load_x(1);
+      }
+      __syncthreads();
+      for (int64_t c = 0; c < nch; ++c) {
+        const bool next = c + 1 < nch;
+        if (next) {
+          store_x(static_cast<int>((c + 1) & 1));
+          if (c + 2 < nch) load_x(c + 2);
+        }
+        if (live) {
+          if (next) load_w(c + 1, c + 1 >= nfull);
+          mult_chunk(static_cast<int>(c & 1));
+          if (next) make_b(c + 1, c + 1 >= nfull);
+        }
+        __syncthreads();
+      }
+    } else if (live) {
+      // ---- resident layers: this wave's chunks q, q + wpb, ...; the W run
+      // and noise of the next one are prepared while the current one
+      // multiplies (no barrier inside).
+      auto mult_res = [&](int64_t c) { multiply(&act[ln * ASTRIDE + c * KC + lh * R], ASTRIDE, PLANE); };
+      int64_t c = q;
+      if (c < nch) {
+        load_w(c, c >= nfull);
+        make_b(c, c >= nfull);
+      }
+      for (; c + wpb < nfull; c += wpb) {
+        load_w(c + wpb, false);
+        mult_res(c);
+        make_b(c + wpb, false);
+      }
+      for (; c < nch; c += wpb) {
+        const bool next = c + wpb < nch;
+        if (next) load_w(c + wpb, c + wpb >= nfull);
+        mult_res(c);
+        if (next) make_b(c + wpb, c + wpb >= nfull);
+      }
+    }
+    __syncthreads();                           // every wave is done reading the activations
+
+    if (wpb > 1) {
+      // partial sums of the waves sharing a block, added in wave order
+      if (live) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int v = 0; v < MF::NACC; ++v) part[((wave * MB + mb) * MF::NACC + v) * 64 + lane] = acc[mb][v];
+      }
+      __syncthreads();
+      if (live && q == 0) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int v = 0; v < MF::NACC; ++v) {
+            float t = part[((wave * MB + mb) * MF::NACC + v) * 64 + lane];
+            for (int u = 1; u < wpb; ++u) t += part[(((wave + u) * MB + mb) * MF::NACC + v) * 64 + lane];
+            acc[mb][v] = t;
+          }
+      }
+      __syncthreads();                         // partial sums consumed
+    }
+
+    if (live && q == 0) {
+      const int64_t j = jbase + ln;
+      float bj = 0.0f;
+      if (p.bias[l] != nullptr && j < out) {
+        const float nz = noise_of_state(state_of(s, static_cast<uint64_t>(p.offset[l] + out * in + j)));
+        bj = __builtin_fmaf(p.sigma, nz, p.bias[l][j]);
+      }
+      int rb = MF::row_base(lane);
+#if defined(__HIP_DEVICE_COMPILE__)
+      // keep the row addresses inside the layer loop (hoisted, they are spilled)
+      asm volatile("" : "+v"(rb));
+#endif
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int v = 0; v < MF::NACC; ++v) {
+          const int row = mb * 32 + rb + MF::row_off(v);
+          float val = acc[mb][v] + bj;
+          if (last) {
+            if (row < batch && j < out) p.y[(i * batch + row) * out + j] = val;
+          } else {
+            if (p.relu) val = val > 0.0f ? val : 0.0f;
+            put(row, static_cast<int>(j), j < out ? val : 0.0f);   // dead columns are the next layer's zero k tail
+          }
+        }
+      }
+    }
+    __syncthreads();                           // the next activations are in place
+  }
+}
+
+hipError_t launch_chain(const ChainParams& p, bool bf16, hipStream_t stream) {
+  if (p.pop > kMaxGridX) return hipErrorInvalidConfiguration;
+  const unsigned grid = static_cast<unsigned>(p.pop);
+  if (bf16)
+    forward_chain_kernel<__bf16, false><<<grid, 512, 0, stream>>>(p);
+  else
+    forward_chain_kernel<float, true><<<grid, 512, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
 template <typename IN_T, bool SPLIT>
 static hipError_t launch_mm_dtype(const FwdParams& p, hipStream_t stream) {
   // <DIM, MB row blocks, NB column blocks per wave, R k per lane per chunk,

@@ -33,6 +33,28 @@ struct GradParams {
   float* out;
 };
 
+// A chain of layers evaluated in one launch (vn_perturbed_mlp).
+constexpr int kChainMaxLayers = 8;
+constexpr int kChainMaxWidth = 256;   // every layer's out (the first layer's in is free)
+constexpr int kChainMaxBatch = 64;
+struct ChainParams {
+  const void* x;                      // (batch, dims[0]) per individual
+  int64_t x_pop_stride;
+  int32_t n_layers;
+  int64_t dims[kChainMaxLayers + 1];
+  const void* w[kChainMaxLayers];     // (dims[l+1], dims[l])
+  const float* bias[kChainMaxLayers]; // may be null
+  int64_t offset[kChainMaxLayers];    // weight-block noise offset of each layer
+  bool relu;                          // ReLU between layers (not after the last)
+  uint32_t wvec;                      // bit l: w[l] takes 16-byte loads
+  bool xvec;                          // x rows take 16-byte loads (aligned, dims[0] and stride whole vectors)
+  const void* seeds;
+  bool seeds_i32;
+  int64_t pop, batch;
+  float sigma, sigma_q;
+  float* y;                           // (pop, batch, dims[n_layers])
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_forward_f32(const FwdParams& p, hipStream_t stream);        // split-bf16 matrix cores
 hipError_t launch_forward_f32_exact(const FwdParams& p, hipStream_t stream);  // fp32 matrix cores
@@ -40,6 +62,7 @@ hipError_t launch_forward_bf16(const FwdParams& p, hipStream_t stream);
 // bf16 operands with the noise formed in floating point (sigma * N): for a
 // sigma too small for sigma * 2^-24 to be a normal float.
 hipError_t launch_forward_bf16_exact(const FwdParams& p, hipStream_t stream);
+hipError_t launch_chain(const ChainParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_gradient(const GradParams& p, hipStream_t stream);
 hipError_t launch_noise(const void* seeds, bool seeds_i32, int64_t pop, int64_t n, int64_t offset,
                         uint32_t* r_out, float* n_out, hipStream_t stream);
