@@ -33,23 +33,28 @@ METRIC = "perturbed-linear TFLOP/s + noise-gradient elements/s, % of roofline, 1
 # ALU roofline of the noise hash on MI355X (gfx950).
 #
 # 256 CUs x 4 SIMDs at 2.4 GHz.  A wave64 VALU instruction occupies a SIMD for
-# 4 / rate cycles, where `rate` is the instruction's issue rate relative to 64
-# lane-ops per CU per clock, measured by virtual_noise_perturbed_amd/vn_probe
+# 4 / rate cycles, where `rate` is the instruction's issue rate per cycle
+# relative to 64 lane-ops per CU, measured by virtual_noise_perturbed_amd/vn_probe
 # (summary in profiles/vn_probe_gfx950.txt).  The hash sequence shipped in
 # every kernel (from the gfx950 assembly of vn_device.hpp) is, per noise
 # element: 1 v_lshl_add_u64 (state step), 2 x [v_lshrrev_b64, 2 v_xor_b32,
-# 2 v_mul_lo_u32, v_mad_u64_u32, v_add3_u32] (xor-shift and 64-bit multiply
-# by GAMMA), v_alignbit_b32 + v_xor_b32 (final xor-shift, low word),
-# v_lshrrev_b32 (r >> 8) and v_cvt_f32_u32.  Its issue cost bounds how many
-# noise elements per second the chip can produce; both kernels need at least
-# this work per element, so it is the peak their rates are compared with.
+# v_mul_lo_u32, 2 v_mad_u64_u32, v_mov_b32] (xor-shift and 64-bit product by
+# GAMMA), v_alignbit_b32 + v_bitop3_b32 (final xor-shift of the low word, with
+# the sign flip), v_ashrrev_i32 (N * 2^24) and v_cvt_f32_i32.  Its issue cost
+# bounds how many noise elements per second the chip can produce; every kernel
+# needs at least this work per element, so it is the peak their rates are
+# compared with.
 N_SIMD = 256 * 4
 CLOCK_HZ = 2.4e9
-PROBE_RATE = {            # measured issue rate, fraction of 64 lane-ops/CU/clk (vn_probe)
-    "v_lshl_add_u64": 0.820, "v_lshrrev_b64": 0.849, "v_xor_b32": 1.273,
-    "v_mul_lo_u32": 0.855, "v_mad_u64_u32": 0.775, "v_mov_b32": 1.419,
-    "v_alignbit_b32": 0.823, "v_bitop3_b32": 1.456, "v_ashrrev_i32": 1.430,
-    "v_cvt_f32_i32": 0.845,
+# Measured issue rate per shader-clock cycle, as a fraction of 64 lane-ops per
+# CU per cycle (vn_probe "rate_per_clock": throughput divided by the shader
+# clock the probe itself read, which moves between 2.0 and 2.43 GHz under
+# load); the peak below prices these per-cycle costs at the nominal 2.4 GHz.
+PROBE_RATE = {
+    "v_lshl_add_u64": 0.885, "v_lshrrev_b64": 0.886, "v_xor_b32": 1.503,
+    "v_mul_lo_u32": 0.838, "v_mad_u64_u32": 0.894, "v_mov_b32": 1.504,
+    "v_alignbit_b32": 0.844, "v_bitop3_b32": 1.616, "v_ashrrev_i32": 1.476,
+    "v_cvt_f32_i32": 0.849,
 }
 HASH_ISA = {              # instructions per noise element: state step, finalizer, N * 2^24 as fp32
     "v_lshl_add_u64": 1, "v_lshrrev_b64": 2, "v_xor_b32": 4, "v_mul_lo_u32": 2,
@@ -328,8 +333,9 @@ def cpu_baseline(wl, budget_s: float):
         "cores": 1,
         "kind": "oracle",
         "sample": (f"numpy oracle, 1 thread: forward of {k} of {wl.pop} individuals through all layers "
-                   f"({t_fwd:.1f} s) and gradients of {m} of {total} flat elements over all {wl.pop} "
-                   f"individuals ({t_grad:.1f} s), scaled to one step ({est_step:.1f} s)"),
+                   f"({t_fwd:.1f} s) and gradients of {m // min(chunk, total)} runs of {min(chunk, total)} flat "
+                   f"elements at random starts (of {total}) over all {wl.pop} individuals ({t_grad:.1f} s), "
+                   f"scaled to one step ({est_step:.1f} s)"),
         "step_s_estimate": est_step,
         "grad_elements_per_s": wl.pop * m / t_grad,
     }

@@ -6,9 +6,12 @@
 // sequence of vn_device.hpp itself, in hashes per second.
 //
 // Each probe kernel runs 16 independent dependency chains per lane (so
-// latency never limits issue) at 8 waves per SIMD; the only memory access
-// is one store per thread of a checksum, into a buffer sized to the grid.
-// Prints one JSON object per line.
+// latency never limits issue) at 8 waves per SIMD; the only memory accesses
+// are one store per thread of a checksum, into a buffer sized to the grid,
+// and two clock readings by thread 0 of block 0.  Those readings (the shader
+// clock counter against the constant 100 MHz reference counter, over block
+// 0's lifetime) give the shader clock the probe ran at, so every rate is also
+// reported per clock cycle.  Prints one JSON object per line.
 
 #include <hip/hip_runtime.h>
 
@@ -30,9 +33,24 @@
 constexpr int kThreads = 256;
 constexpr int kChains = 16;
 
+// Shader-clock and reference-clock counters at the start and end of block 0.
+#define CLOCK_BEGIN                                                                     \
+  uint64_t clk_t0 = 0, clk_r0 = 0;                                                      \
+  if (blockIdx.x == 0 && threadIdx.x == 0) {                                            \
+    clk_t0 = __builtin_amdgcn_s_memtime();                                              \
+    clk_r0 = __builtin_amdgcn_s_memrealtime();                                          \
+  }
+#define CLOCK_END                                                                       \
+  if (blockIdx.x == 0 && threadIdx.x == 0) {                                            \
+    const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime(); \
+    clk[0] = t1 - clk_t0;                                                               \
+    clk[1] = r1 - clk_r0;                                                               \
+  }
+
 // 32-bit ops: a = op(a, b[, b2]) on 16 chains.
 #define PROBE32(NAME, ASM)                                                              \
-  __global__ __launch_bounds__(kThreads) void NAME(uint32_t* out, int iters, uint32_t seed) { \
+  __global__ __launch_bounds__(kThreads) void NAME(uint32_t* out, uint64_t* clk, int iters, uint32_t seed) { \
+    CLOCK_BEGIN                                                                         \
     uint32_t a[kChains];                                                                \
     const uint32_t b = seed * 2654435761u + threadIdx.x;                                \
     const uint32_t b2 = seed ^ (threadIdx.x * 40503u);                                  \
@@ -42,12 +60,14 @@ constexpr int kChains = 16;
     }                                                                                   \
     uint32_t r = 0;                                                                     \
     _Pragma("unroll") for (int c = 0; c < kChains; ++c) r ^= a[c];                      \
+    CLOCK_END                                                                           \
     out[blockIdx.x * kThreads + threadIdx.x] = r;                                       \
   }
 
 // 64-bit ops on 16 chains of register pairs (%1: 64-bit operand, %2, %3: 32-bit operands).
 #define PROBE64(NAME, ASM)                                                              \
-  __global__ __launch_bounds__(kThreads) void NAME(uint32_t* out, int iters, uint32_t seed) { \
+  __global__ __launch_bounds__(kThreads) void NAME(uint32_t* out, uint64_t* clk, int iters, uint32_t seed) { \
+    CLOCK_BEGIN                                                                         \
     uint64_t a[kChains];                                                                \
     const uint64_t b = (static_cast<uint64_t>(seed) << 32) | threadIdx.x;               \
     const uint32_t b1 = seed * 2654435761u + threadIdx.x, b2 = seed ^ 0x9E3779B9u;      \
@@ -58,6 +78,7 @@ constexpr int kChains = 16;
     }                                                                                   \
     uint64_t r = 0;                                                                     \
     _Pragma("unroll") for (int c = 0; c < kChains; ++c) r ^= a[c];                      \
+    CLOCK_END                                                                           \
     out[blockIdx.x * kThreads + threadIdx.x] = static_cast<uint32_t>(r ^ (r >> 32));    \
   }
 
@@ -84,7 +105,8 @@ PROBE64(p_shr64, "v_lshrrev_b64 %0, 30, %0")
 PROBE64(p_add64, "v_lshl_add_u64 %0, %0, 0, %1")
 
 // The shipped hash: Weyl-stepped states, low 32 bits of the finalizer.
-__global__ __launch_bounds__(kThreads) void p_hash(uint32_t* out, int iters, uint32_t seed) {
+__global__ __launch_bounds__(kThreads) void p_hash(uint32_t* out, uint64_t* clk, int iters, uint32_t seed) {
+  CLOCK_BEGIN
   constexpr int S = 8;
   uint64_t z[S];
   const uint64_t g = blockIdx.x * kThreads + threadIdx.x;
@@ -98,12 +120,14 @@ __global__ __launch_bounds__(kThreads) void p_hash(uint32_t* out, int iters, uin
       z[c] += vn::gamma_times(S);
     }
   }
+  CLOCK_END
   out[g] = acc;
 }
 
 // The same hash written as plain 64-bit C (z * GAMMA), for comparison with
 // the library's word-level form.
-__global__ __launch_bounds__(kThreads) void p_hash_plain(uint32_t* out, int iters, uint32_t seed) {
+__global__ __launch_bounds__(kThreads) void p_hash_plain(uint32_t* out, uint64_t* clk, int iters, uint32_t seed) {
+  CLOCK_BEGIN
   constexpr int S = 8;
   uint64_t z[S];
   const uint64_t g = blockIdx.x * kThreads + threadIdx.x;
@@ -120,18 +144,21 @@ __global__ __launch_bounds__(kThreads) void p_hash_plain(uint32_t* out, int iter
       z[c] += vn::gamma_times(S);
     }
   }
+  CLOCK_END
   out[g] = acc;
 }
 
 // MFMA / VALU co-execution: per loop slot, one MFMA (or none) and NV integer
 // multiplies on 8 independent chains; 2 waves per SIMD.  If a shape's MFMAs
-// run beside the VALU, slot cycles stay near the VALU-only figure.
+// run beside the VALU, slot cycles (launch time at the measured shader clock)
+// stay near the VALU-only figure.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 template <int SHAPE, int NV>
-__global__ __launch_bounds__(kThreads) void p_coexec(uint32_t* out, int iters, uint32_t seed) {
+__global__ __launch_bounds__(kThreads) void p_coexec(uint32_t* out, uint64_t* clk, int iters, uint32_t seed) {
+  CLOCK_BEGIN
   f32x16 A0 = {}, A1 = {};
   f32x4 B0 = {}, B1 = {};
   const float a = threadIdx.x * 1e-3f, b = 1.0001f;
@@ -171,18 +198,19 @@ __global__ __launch_bounds__(kThreads) void p_coexec(uint32_t* out, int iters, u
   uint32_t x = 0;
 #pragma unroll
   for (int c = 0; c < 8; ++c) x ^= v[c];
+  CLOCK_END
   out[blockIdx.x * kThreads + threadIdx.x] = x ^ __builtin_bit_cast(uint32_t, sacc);
 }
 
 struct CoProbe {
   const char* name;
-  void (*fn)(uint32_t*, int, uint32_t);
+  void (*fn)(uint32_t*, uint64_t*, int, uint32_t);
   int nv;
 };
 
 struct Probe {
   const char* name;
-  void (*fn)(uint32_t*, int, uint32_t);
+  void (*fn)(uint32_t*, uint64_t*, int, uint32_t);
   int per_iter;   // instructions (or hashes) per lane per iteration
   const char* what;
 };
@@ -202,6 +230,8 @@ int main(int argc, char** argv) {
               prop.name, prop.gcnArchName, cus, clock_khz / 1e3, blocks, kThreads, iters);
   uint32_t* out = nullptr;
   CHECK(hipMalloc(&out, sizeof(uint32_t) * blocks * kThreads));
+  uint64_t* clk = nullptr;
+  CHECK(hipMalloc(&clk, sizeof(uint64_t) * 2));
   hipEvent_t e0, e1;
   CHECK(hipEventCreate(&e0));
   CHECK(hipEventCreate(&e1));
@@ -233,27 +263,36 @@ int main(int argc, char** argv) {
   const double peak_lane_ops = static_cast<double>(cus) * 64.0 * clock_khz * 1e3;
   for (const Probe& pr : probes) {
     // warm-up, then the best of 3 timed launches
-    pr.fn<<<blocks, kThreads>>>(out, iters / 8, 1u);
+    pr.fn<<<blocks, kThreads>>>(out, clk, iters / 8, 1u);
     CHECK(hipGetLastError());
     CHECK(hipDeviceSynchronize());
     float best = 1e30f;
+    double ghz = 0.0;   // shader clock of the best launch
     for (int rep = 0; rep < 3; ++rep) {
       CHECK(hipEventRecord(e0));
-      pr.fn<<<blocks, kThreads>>>(out, iters, 2u + rep);
+      pr.fn<<<blocks, kThreads>>>(out, clk, iters, 2u + rep);
       CHECK(hipEventRecord(e1));
       CHECK(hipEventSynchronize(e1));
       float ms = 0;
       CHECK(hipEventElapsedTime(&ms, e0, e1));
-      if (ms < best) best = ms;
+      uint64_t c[2];
+      CHECK(hipMemcpy(c, clk, sizeof(c), hipMemcpyDeviceToHost));
+      if (ms < best) {
+        best = ms;
+        ghz = c[1] > 0 ? static_cast<double>(c[0]) / (static_cast<double>(c[1]) / 100e6) / 1e9 : 0.0;
+      }
     }
     const double ops = static_cast<double>(blocks) * kThreads * iters * pr.per_iter;
     const double rate = ops / (best * 1e-3);
+    const double per_clk = static_cast<double>(cus) * 64.0 * ghz * 1e9;   // full-rate lane-ops at that clock
     if (std::strcmp(pr.what, "hash") == 0) {
-      std::printf("{\"probe\": \"%s\", \"ms\": %.4f, \"hashes_per_s\": %.4e, \"lane_cycles_per_hash\": %.2f}\n", pr.name,
-                  best, rate, peak_lane_ops / rate);
+      std::printf("{\"probe\": \"%s\", \"ms\": %.4f, \"hashes_per_s\": %.4e, \"lane_cycles_per_hash\": %.2f, "
+                  "\"shader_ghz\": %.3f, \"lane_cycles_per_hash_at_that_clock\": %.2f}\n",
+                  pr.name, best, rate, peak_lane_ops / rate, ghz, per_clk / rate);
     } else {
-      std::printf("{\"probe\": \"%s\", \"ms\": %.4f, \"lane_ops_per_s\": %.4e, \"rate_vs_full\": %.3f}\n", pr.name,
-                  best, rate, rate / peak_lane_ops);
+      std::printf("{\"probe\": \"%s\", \"ms\": %.4f, \"lane_ops_per_s\": %.4e, \"rate_vs_full\": %.3f, "
+                  "\"shader_ghz\": %.3f, \"rate_per_clock\": %.3f}\n",
+                  pr.name, best, rate, rate / peak_lane_ops, ghz, rate / per_clk);
     }
     std::fflush(stdout);
   }
@@ -268,25 +307,34 @@ int main(int argc, char** argv) {
   const int co_blocks = cus * 2;   // 2 blocks of 4 waves per CU = 2 waves per SIMD
   const int co_iters = 10000;
   for (const CoProbe& pr : co) {
-    pr.fn<<<co_blocks, kThreads>>>(out, co_iters / 8, 1u);
+    pr.fn<<<co_blocks, kThreads>>>(out, clk, co_iters / 8, 1u);
     CHECK(hipGetLastError());
     CHECK(hipDeviceSynchronize());
     float best = 1e30f;
+    double ghz = 0.0;   // shader clock of the best launch
     for (int rep = 0; rep < 3; ++rep) {
       CHECK(hipEventRecord(e0));
-      pr.fn<<<co_blocks, kThreads>>>(out, co_iters, 2u + rep);
+      pr.fn<<<co_blocks, kThreads>>>(out, clk, co_iters, 2u + rep);
       CHECK(hipEventRecord(e1));
       CHECK(hipEventSynchronize(e1));
       float ms = 0;
       CHECK(hipEventElapsedTime(&ms, e0, e1));
-      if (ms < best) best = ms;
+      uint64_t c[2];
+      CHECK(hipMemcpy(c, clk, sizeof(c), hipMemcpyDeviceToHost));
+      if (ms < best) {
+        best = ms;
+        ghz = c[1] > 0 ? static_cast<double>(c[0]) / (static_cast<double>(c[1]) / 100e6) / 1e9 : 0.0;
+      }
     }
-    const double simd_cycles = best * 1e-3 * clock_khz * 1e3;
+    // launch time at the measured clock, over the slots one SIMD issues
+    const double simd_cycles = best * 1e-3 * ghz * 1e9;
     const double slots_per_simd = 2.0 * co_iters * 2.0;  // 2 slots per iteration, 2 waves per SIMD
-    std::printf("{\"coexec\": \"%s\", \"v_mul_lo_u32_per_slot\": %d, \"ms\": %.4f, \"simd_cycles_per_slot\": %.2f}\n",
-                pr.name, pr.nv, best, simd_cycles / slots_per_simd);
+    std::printf("{\"coexec\": \"%s\", \"v_mul_lo_u32_per_slot\": %d, \"ms\": %.4f, \"shader_ghz\": %.3f, "
+                "\"simd_cycles_per_slot\": %.2f}\n",
+                pr.name, pr.nv, best, ghz, simd_cycles / slots_per_simd);
     std::fflush(stdout);
   }
+  CHECK(hipFree(clk));
   CHECK(hipFree(out));
   return 0;
 }
