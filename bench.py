@@ -32,37 +32,21 @@ METRIC = "perturbed-linear TFLOP/s + noise-gradient elements/s, % of roofline, 1
 # ---------------------------------------------------------------------------
 # ALU roofline of the noise hash on MI355X (gfx950).
 #
-# 256 CUs x 4 SIMDs at 2.4 GHz.  A wave64 VALU instruction occupies a SIMD for
-# 4 / rate cycles, where `rate` is the instruction's issue rate per cycle
-# relative to 64 lane-ops per CU, measured by virtual_noise_perturbed_amd/vn_probe
-# (summary in profiles/vn_probe_gfx950.txt).  The hash sequence shipped in
-# every kernel (from the gfx950 assembly of vn_device.hpp) is, per noise
-# element: 1 v_lshl_add_u64 (state step), 2 x [v_lshrrev_b64, 2 v_xor_b32,
-# v_mul_lo_u32, 2 v_mad_u64_u32, v_mov_b32] (xor-shift and 64-bit product by
-# GAMMA), v_alignbit_b32 + v_bitop3_b32 (final xor-shift of the low word, with
-# the sign flip), v_ashrrev_i32 (N * 2^24) and v_cvt_f32_i32.  Its issue cost
-# bounds how many noise elements per second the chip can produce; every kernel
-# needs at least this work per element, so it is the peak their rates are
-# compared with.
-N_SIMD = 256 * 4
+# Every kernel has to produce each noise element: the state step, the
+# finalizer (2 x [v_lshrrev_b64, 2 v_xor_b32, v_mul_lo_u32, 2 v_mad_u64_u32,
+# v_mov_b32], then v_alignbit_b32 + v_bitop3_b32 for the low word with the
+# sign flip), v_ashrrev_i32 for N * 2^24 and v_cvt_f32_i32 -- and consume it
+# with at least one fma.  virtual_noise_perturbed_amd/vn_probe measures that
+# exact sequence ("noise_fma": eight independent Weyl-stepped chains per lane,
+# 8 waves per SIMD, nothing else) and reads the shader clock of the launch
+# (which moves between 2.0 and 2.43 GHz under load): 17.23 lane-cycles per
+# element per CU (summary in profiles/vn_probe_gfx950.txt).  The peak prices
+# that per-cycle cost at the nominal 2.4 GHz on 256 CUs x 64 lanes.  (Summing
+# the instructions' isolated issue costs gives 17.9: mixed, they overlap a
+# little.)
 CLOCK_HZ = 2.4e9
-# Measured issue rate per shader-clock cycle, as a fraction of 64 lane-ops per
-# CU per cycle (vn_probe "rate_per_clock": throughput divided by the shader
-# clock the probe itself read, which moves between 2.0 and 2.43 GHz under
-# load); the peak below prices these per-cycle costs at the nominal 2.4 GHz.
-PROBE_RATE = {
-    "v_lshl_add_u64": 0.885, "v_lshrrev_b64": 0.886, "v_xor_b32": 1.503,
-    "v_mul_lo_u32": 0.838, "v_mad_u64_u32": 0.894, "v_mov_b32": 1.504,
-    "v_alignbit_b32": 0.844, "v_bitop3_b32": 1.616, "v_ashrrev_i32": 1.476,
-    "v_cvt_f32_i32": 0.849,
-}
-HASH_ISA = {              # instructions per noise element: state step, finalizer, N * 2^24 as fp32
-    "v_lshl_add_u64": 1, "v_lshrrev_b64": 2, "v_xor_b32": 4, "v_mul_lo_u32": 2,
-    "v_mad_u64_u32": 4, "v_mov_b32": 2, "v_alignbit_b32": 1, "v_bitop3_b32": 1,
-    "v_ashrrev_i32": 1, "v_cvt_f32_i32": 1,
-}
-HASH_SIMD_CYCLES = sum(n * 4.0 / PROBE_RATE[k] for k, n in HASH_ISA.items())   # per wave64 element
-HASH_PEAK_PER_S = N_SIMD * 64 * CLOCK_HZ / HASH_SIMD_CYCLES
+NOISE_LANE_CYCLES = 17.23   # per element per CU lane, at the measured clock (vn_probe noise_fma)
+HASH_PEAK_PER_S = 256 * 64 * CLOCK_HZ / NOISE_LANE_CYCLES
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK = 2.5e15    # dense bf16 matrix-core FLOP/s
 
@@ -455,8 +439,9 @@ def main():
             "traffic": traffic,
             "units_per_launch": units,
             "avg_launch_ms": round(avg_ms[dom], 4),
-            "peak_basis": (f"hash issue bound: {HASH_SIMD_CYCLES:.1f} SIMD-cycles per wave64 element "
-                           f"(ISA count x measured issue costs), {N_SIMD} SIMDs x 64 lanes x 2.4 GHz"),
+            "peak_basis": (f"noise generation bound: {NOISE_LANE_CYCLES} lane-cycles per noise element "
+                           f"(state step, hash, N as fp32, one fma; measured per shader-clock cycle), "
+                           f"256 CUs x 64 lanes x 2.4 GHz"),
         }
 
     value = flops_of(wl) / (ms_per_step * 1e-3) / 1e12

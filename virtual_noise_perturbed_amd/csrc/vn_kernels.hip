@@ -1374,10 +1374,12 @@ hipError_t launch_forward_bf16_exact(const FwdParams& p, hipStream_t stream) {
 
 // ---------------------------------------------------------------------------
 // Gradient, element-major: grad[t] = scale * sum_i f_i noise_i[offset + t].
-// Lane owns E consecutive elements; wave w walks its quarter of the population.
-// The sums run over the integers N * 2^24 and take the 2^-24 at the end: a
-// power-of-two factor, so every rounding is the one of the sum over N.
-template <int E>
+// Lane owns E consecutive elements; wave w walks its quarter of the population
+// in groups of four individuals, whose seeds and fitness values (wave-uniform,
+// scalar loads) are fetched one group ahead.  The sums run over the integers
+// N * 2^24 and take the 2^-24 at the end: a power-of-two factor, so every
+// rounding is the one of the sum over N.
+template <int E, bool SEEDS_I32>
 __global__ __launch_bounds__(256) void grad_elem_kernel(GradParams p, int64_t n_blocks) {
   __shared__ float red[4][64 * E];
   const int lane = threadIdx.x & 63;
@@ -1385,6 +1387,14 @@ __global__ __launch_bounds__(256) void grad_elem_kernel(GradParams p, int64_t n_
   const int64_t q = p.pop / 4, r = p.pop % 4;
   const int64_t i_begin = wave * q + (wave < r ? wave : r);
   const int64_t i_end = i_begin + q + (wave < r ? 1 : 0);
+  // Nothing the kernel writes aliases the inputs: lets the compiler use scalar loads.
+  const float* __restrict__ fitness = p.fitness;
+  const int64_t* __restrict__ seeds64 = static_cast<const int64_t*>(p.seeds);
+  const int32_t* __restrict__ seeds32 = static_cast<const int32_t*>(p.seeds);
+  float* __restrict__ out = p.out;
+  auto seed = [&](int64_t i) -> uint64_t {
+    return SEEDS_I32 ? static_cast<uint64_t>(static_cast<int64_t>(seeds32[i])) : static_cast<uint64_t>(seeds64[i]);
+  };
 
   for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
     const int64_t e0 = blk * (64 * E) + lane * E;
@@ -1398,18 +1408,38 @@ __global__ __launch_bounds__(256) void grad_elem_kernel(GradParams p, int64_t n_
       acc[e] = 0.0f;
     }
     int64_t i = i_begin;
-    for (; i + 4 <= i_end; i += 4) {
+    uint64_t sn[4];
+    float fn[4];
+    if (i + 4 <= i_end) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint64_t s = load_seed(p.seeds, p.seeds_i32, i + u);
-        const float f = p.fitness[i + u];
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(f, static_cast<float>(centered_q(s + c[e])), acc[e]);
+        sn[u] = seed(i + u);
+        fn[u] = fitness[i + u];
       }
     }
+    for (; i + 4 <= i_end; i += 4) {
+      uint64_t sc[4];
+      float fc[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sc[u] = sn[u];
+        fc[u] = fn[u];
+      }
+      if (i + 8 <= i_end) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          sn[u] = seed(i + 4 + u);
+          fn[u] = fitness[i + 4 + u];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(fc[u], static_cast<float>(centered_q(sc[u] + c[e])), acc[e]);
+    }
     for (; i < i_end; ++i) {
-      const uint64_t s = load_seed(p.seeds, p.seeds_i32, i);
-      const float f = p.fitness[i];
+      const uint64_t s = seed(i);
+      const float f = fitness[i];
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(f, static_cast<float>(centered_q(s + c[e])), acc[e]);
     }
@@ -1421,11 +1451,21 @@ __global__ __launch_bounds__(256) void grad_elem_kernel(GradParams p, int64_t n_
       for (int e = 0; e < E; ++e) {
         const int k = lane * E + e;
         const float v = ((red[0][k] + red[1][k]) + red[2][k]) + red[3][k];
-        if (e0 + e < p.n) p.out[e0 + e] = (v * 0x1p-24f) * p.scale;
+        if (e0 + e < p.n) out[e0 + e] = (v * 0x1p-24f) * p.scale;
       }
     }
     __syncthreads();
   }
+}
+
+template <int E>
+static void launch_grad_elem(const GradParams& p, hipStream_t stream) {
+  const int64_t n_blocks = (p.n + 64 * E - 1) / (64 * E);
+  const int64_t g = n_blocks < kMaxGridX ? n_blocks : kMaxGridX;
+  if (p.seeds_i32)
+    grad_elem_kernel<E, true><<<static_cast<unsigned>(g), 256, 0, stream>>>(p, n_blocks);
+  else
+    grad_elem_kernel<E, false><<<static_cast<unsigned>(g), 256, 0, stream>>>(p, n_blocks);
 }
 
 // Gradient, population-major: one wave per element, lanes own individuals.
@@ -1451,13 +1491,9 @@ hipError_t launch_gradient(const GradParams& p, hipStream_t stream) {
     blocks = blocks < 65536 ? blocks : 65536;
     grad_pop_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(p);
   } else if (p.n < (int64_t(1) << 20)) {
-    const int64_t n_blocks = (p.n + 63) / 64;
-    const int64_t g = n_blocks < kMaxGridX ? n_blocks : kMaxGridX;
-    grad_elem_kernel<1><<<static_cast<unsigned>(g), 256, 0, stream>>>(p, n_blocks);
+    launch_grad_elem<1>(p, stream);
   } else {
-    const int64_t n_blocks = (p.n + 255) / 256;
-    const int64_t g = n_blocks < kMaxGridX ? n_blocks : kMaxGridX;
-    grad_elem_kernel<4><<<static_cast<unsigned>(g), 256, 0, stream>>>(p, n_blocks);
+    launch_grad_elem<4>(p, stream);
   }
   return hipGetLastError();
 }

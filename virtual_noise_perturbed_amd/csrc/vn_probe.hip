@@ -2,8 +2,10 @@
 //
 // Measures (1) the issue rate of every vector instruction the hash sequence
 // uses, as lane-operations per second and as a fraction of the full 32-bit
-// rate (64 lane-ops per CU per clock), and (2) the throughput of the hash
-// sequence of vn_device.hpp itself, in hashes per second.
+// rate (64 lane-ops per CU per clock), (2) the throughput of the hash
+// sequence of vn_device.hpp itself, in hashes per second, and (3) that of
+// whole noise elements as the kernels consume them (state step, hash, N * 2^24
+// as fp32, one fma into an accumulator).
 //
 // Each probe kernel runs 16 independent dependency chains per lane (so
 // latency never limits issue) at 8 waves per SIMD; the only memory accesses
@@ -148,6 +150,35 @@ __global__ __launch_bounds__(kThreads) void p_hash_plain(uint32_t* out, uint64_t
   out[g] = acc;
 }
 
+// Noise elements as every kernel consumes them: Weyl-stepped states, N * 2^24
+// as fp32 (centered_q and the conversion), each folded into an fp32
+// accumulator by one fma (eight independent accumulators per lane).
+__global__ __launch_bounds__(kThreads) void p_noise(uint32_t* out, uint64_t* clk, int iters, uint32_t seed) {
+  CLOCK_BEGIN
+  constexpr int S = 8;
+  uint64_t z[S];
+  float acc[S];
+  const uint64_t g = blockIdx.x * kThreads + threadIdx.x;
+  const float f = 1.0f + static_cast<float>(seed) * 1e-3f;
+#pragma unroll
+  for (int c = 0; c < S; ++c) {
+    z[c] = vn::state_of(seed, g * 64 + c);
+    acc[c] = 0.0f;
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < S; ++c) {
+      acc[c] = __builtin_fmaf(f, static_cast<float>(vn::centered_q(z[c])), acc[c]);
+      z[c] += vn::gamma_times(S);
+    }
+  }
+  float t = 0.0f;
+#pragma unroll
+  for (int c = 0; c < S; ++c) t += acc[c];
+  CLOCK_END
+  out[g] = __builtin_bit_cast(uint32_t, t);
+}
+
 // MFMA / VALU co-execution: per loop slot, one MFMA (or none) and NV integer
 // multiplies on 8 independent chains; 2 waves per SIMD.  If a shape's MFMAs
 // run beside the VALU, slot cycles (launch time at the measured shader clock)
@@ -259,6 +290,7 @@ int main(int argc, char** argv) {
       {"v_lshl_add_u64", p_add64, kChains, "64-bit"},
       {"hash", p_hash, 8, "hash"},
       {"hash_plain", p_hash_plain, 8, "hash"},
+      {"noise_fma", p_noise, 8, "hash"},
   };
   const double peak_lane_ops = static_cast<double>(cus) * 64.0 * clock_khz * 1e3;
   for (const Probe& pr : probes) {
