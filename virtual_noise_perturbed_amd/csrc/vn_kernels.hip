@@ -329,9 +329,6 @@ __global__ __launch_bounds__(64 * WPG, WAVES) void forward_mm_kernel(FwdParams p
   constexpr int SEG_PER_THREAD = (NSEG + NTHR - 1) / NTHR;
   constexpr uint64_t kChunkStep = gamma_times(KC);
   static_assert(!SPLIT || sizeof(IN_T) == 4, "split is for fp32 operands");
-  constexpr int kMfmaPerChunk = T * MB * NB * (SPLIT ? 3 : 1);
-  // about 23 VALU instructions per noise element (+3 for the split)
-  constexpr int kValuPerMfma = (NB * R * (SPLIT ? 26 : 23)) / kMfmaPerChunk;
 
   __shared__ __attribute__((aligned(16))) __bf16 lds[2 * BUF];
 
@@ -518,6 +515,51 @@ __global__ __launch_bounds__(64 * WPG, WAVES) void forward_mm_kernel(FwdParams p
     }
   };
 
+  // Steady-state chunk: the noise of chunk c+1 and the MFMAs of chunk c,
+  // interleaved by hand.  Each MFMA is fenced between scheduling barriers
+  // with its share of the noise work in front of it, so consecutive MFMAs on
+  // one accumulator sit a few hundred VALU cycles apart: the wave never waits
+  // on the previous MFMA and the matrix cores run under the hash.  The A
+  // fragments of the next (k-step, row block) are read from LDS while the
+  // current one's MFMAs issue.
+  auto noise_and_multiply = [&](int buf, float (&nz)[NB][R]) {
+    constexpr int G = T * MB;                     // (k-step, row block) groups
+    constexpr int PER_G = NB * (SPLIT ? 3 : 1);   // MFMAs per group
+    constexpr int NM = G * PER_G;
+    constexpr int NE = NB * R;                    // noise elements per lane
+    const __bf16* abase = &lds[buf * BUF + ln * STRIDE + lh * R];
+    bf16x8 ah[2], al[2];
+    auto read_a = [&](int g) {
+      const int t = g / MB, mb = g % MB;
+      ah[g & 1] = *reinterpret_cast<const bf16x8*>(abase + mb * DIM * STRIDE + t * 8);
+      if constexpr (SPLIT) al[g & 1] = *reinterpret_cast<const bf16x8*>(abase + PLANE + mb * DIM * STRIDE + t * 8);
+    };
+    read_a(0);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int g = m / PER_G, w = m % PER_G;
+      const int nb = w / (SPLIT ? 3 : 1), term = w % (SPLIT ? 3 : 1);
+      const int t = g / MB, mb = g % MB;
+      if (w == 0 && g + 1 < G) read_a(g + 1);
+#pragma unroll
+      for (int e = m * NE / NM; e < (m + 1) * NE / NM; ++e)
+        nz[e / R][e % R] = static_cast<float>(centered_q(z[e / R] + gamma_times(e % R)));
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 bfh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&bh[nb][t * 4]));
+      if constexpr (SPLIT) {
+        const bf16x8 bfl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&bl[nb][t * 4]));
+        if (term == 0) acc[mb][nb] = mfma_bf16<DIM>(al[g & 1], bfh, acc[mb][nb]);
+        if (term == 1) acc[mb][nb] = mfma_bf16<DIM>(ah[g & 1], bfl, acc[mb][nb]);
+        if (term == 2) acc[mb][nb] = mfma_bf16<DIM>(ah[g & 1], bfh, acc[mb][nb]);
+      } else {
+        acc[mb][nb] = mfma_bf16<DIM>(ah[g & 1], bfh, acc[mb][nb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) z[nb] += kChunkStep;
+  };
+
   // A wave whose columns all lie past `out` (narrow layers) only helps stage
   // X and joins the barriers: no noise, no matrix work.
   const bool live = jbase < out;
@@ -542,16 +584,8 @@ __global__ __launch_bounds__(64 * WPG, WAVES) void forward_mm_kernel(FwdParams p
     if (live) {
       load_w(c + 1, false);
       float nz[NB][R];
-      make_noise(nz);
-      multiply(static_cast<int>(c & 1));
+      noise_and_multiply(static_cast<int>(c & 1), nz);
       make_b(nz, c + 1, false);
-      // Interleave: one MFMA, then a share of the noise VALU work, repeatedly,
-      // so the matrix cores run under the hash instead of after it.
-#pragma unroll
-      for (int k = 0; k < kMfmaPerChunk; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
-      }
     }
     __syncthreads();
   }
