@@ -39,13 +39,14 @@ METRIC = "perturbed-linear TFLOP/s + noise-gradient elements/s, % of roofline, 1
 # with at least one fma.  virtual_noise_perturbed_amd/vn_probe measures that
 # exact sequence ("noise_fma": eight independent Weyl-stepped chains per lane,
 # 8 waves per SIMD, nothing else) and reads the shader clock of the launch
-# (which moves between 2.0 and 2.43 GHz under load): 17.23 lane-cycles per
-# element per CU (summary in profiles/vn_probe_gfx950.txt).  The peak prices
+# (which moves between 2.0 and 2.43 GHz under load): 16.96 to 17.53
+# lane-cycles per element per CU over runs, the lowest taken (summary in
+# profiles/vn_probe_gfx950.txt).  The peak prices
 # that per-cycle cost at the nominal 2.4 GHz on 256 CUs x 64 lanes.  (Summing
 # the instructions' isolated issue costs gives 17.9: mixed, they overlap a
 # little.)
 CLOCK_HZ = 2.4e9
-NOISE_LANE_CYCLES = 17.23   # per element per CU lane, at the measured clock (vn_probe noise_fma)
+NOISE_LANE_CYCLES = 16.96   # per element per CU lane, at the measured clock (vn_probe noise_fma)
 HASH_PEAK_PER_S = 256 * 64 * CLOCK_HZ / NOISE_LANE_CYCLES
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK = 2.5e15    # dense bf16 matrix-core FLOP/s

@@ -102,6 +102,9 @@ PROBE32(p_ashr, "v_ashrrev_i32 %0, 8, %0")
 PROBE32(p_cvt_i32, "v_cvt_f32_i32 %0, %0")
 PROBE32(p_cvt_ubyte, "v_cvt_f32_ubyte2 %0, %0")
 PROBE32(p_perm, "v_perm_b32 %0, %0, %1, %1")
+PROBE32(p_cvt_pk_bf16, "v_cvt_pk_bf16_f32 %0, %0, %1")
+PROBE32(p_sub_f32, "v_sub_f32 %0, %0, %1")
+PROBE32(p_and, "v_and_b32 %0, %0, %1")
 PROBE64(p_mad64, "v_mad_u64_u32 %0, vcc, %2, %3, %0")
 PROBE64(p_shr64, "v_lshrrev_b64 %0, 30, %0")
 PROBE64(p_add64, "v_lshl_add_u64 %0, %0, 0, %1")
@@ -285,6 +288,9 @@ int main(int argc, char** argv) {
       {"v_cvt_f32_i32", p_cvt_i32, kChains, "32-bit"},
       {"v_cvt_f32_ubyte2", p_cvt_ubyte, kChains, "32-bit"},
       {"v_perm_b32", p_perm, kChains, "32-bit"},
+      {"v_cvt_pk_bf16_f32", p_cvt_pk_bf16, kChains, "32-bit"},
+      {"v_sub_f32", p_sub_f32, kChains, "32-bit"},
+      {"v_and_b32", p_and, kChains, "32-bit"},
       {"v_mad_u64_u32", p_mad64, kChains, "64-bit"},
       {"v_lshrrev_b64", p_shr64, kChains, "64-bit"},
       {"v_lshl_add_u64", p_add64, kChains, "64-bit"},
