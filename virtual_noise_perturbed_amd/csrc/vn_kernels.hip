@@ -741,7 +741,7 @@ __global__ __launch_bounds__(512, 1) void forward_rows_kernel(FwdParams p, int64
   IN_T xr[MBW][T][8];                     // X of the chunk being loaded
   uint32_t ah[MBW][T][4], al[MBW][T][4];  // packed A fragments of the chunk being multiplied
 
-  auto load = [&](int64_t c, bool guarded) {
+  auto load_w = [&](int64_t c, bool guarded) {
     const int64_t k0 = c * KC;
     if (!guarded) {
       if constexpr (RB * sizeof(IN_T) >= 16) {
@@ -750,18 +750,21 @@ __global__ __launch_bounds__(512, 1) void forward_rows_kernel(FwdParams p, int64
         const uint2 v = *reinterpret_cast<const uint2*>(wsrc + k0);
         __builtin_memcpy(wv, &v, 8);
       }
-#pragma unroll
-      for (int mb = 0; mb < MBW; ++mb)
-#pragma unroll
-        for (int t = 0; t < T; ++t) load_run<IN_T, 8, true>(xr[mb][t], xrow[mb] + k0 + t * 16);
     } else {
       load_run_guarded<IN_T, RB>(wv, wsrc + k0, static_cast<int>(in - k0 - gk));
-#pragma unroll
-      for (int mb = 0; mb < MBW; ++mb)
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-          load_run_guarded<IN_T, 8>(xr[mb][t], xrow[mb] + k0 + t * 16, static_cast<int>(in - k0 - t * 16 - lh * 8));
     }
+  };
+  auto load_x = [&](int64_t c, bool guarded) {
+    const int64_t k0 = c * KC;
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        if (!guarded)
+          load_run<IN_T, 8, true>(xr[mb][t], xrow[mb] + k0 + t * 16);
+        else
+          load_run_guarded<IN_T, 8>(xr[mb][t], xrow[mb] + k0 + t * 16, static_cast<int>(in - k0 - t * 16 - lh * 8));
+      }
   };
   // W + sigma N of the thread's run -> LDS buffer `buf` (hi, and lo when split).
   auto make_tile = [&](int buf) {
@@ -839,19 +842,25 @@ __global__ __launch_bounds__(512, 1) void forward_rows_kernel(FwdParams p, int64
       }
   };
 
-  // Software pipeline: iteration c loads chunk c+1, builds its tile in the
-  // other LDS buffer while the matrix cores work on chunk c, then packs the
-  // loaded X into the A fragments of chunk c+1; one barrier per iteration.
+  // Software pipeline: iteration c loads X of chunk c+1, builds the tile of
+  // chunk c+1 in the other LDS buffer from the W run loaded one iteration
+  // earlier and loads the W run of chunk c+2, while the matrix cores work on
+  // chunk c; then it packs the X of chunk c+1 into the A fragments.  One
+  // barrier per iteration.  (Loading W in the same iteration as its tile left
+  // every tile build waiting on a global load.)
   if (nchunks > 0) {
-    load(0, nfull == 0);
+    load_w(0, nfull == 0);
+    load_x(0, nfull == 0);
     make_tile(0);
     make_a();
+    if (nchunks > 1) load_w(1, nfull <= 1);
   }
   __syncthreads();
   int64_t c = 0;
-  for (; c + 1 < nfull; ++c) {
-    load(c + 1, false);
+  for (; c + 2 < nfull; ++c) {
+    load_x(c + 1, false);
     make_tile(static_cast<int>((c + 1) & 1));
+    load_w(c + 2, false);
     if (live) {
       multiply(static_cast<int>(c & 1));
 #pragma unroll
@@ -866,8 +875,9 @@ __global__ __launch_bounds__(512, 1) void forward_rows_kernel(FwdParams p, int64
   for (; c < nchunks; ++c) {
     const bool next = c + 1 < nchunks;
     if (next) {
-      load(c + 1, c + 1 >= nfull);
+      load_x(c + 1, c + 1 >= nfull);
       make_tile(static_cast<int>((c + 1) & 1));
+      if (c + 2 < nchunks) load_w(c + 2, c + 2 >= nfull);
     }
     if (live) multiply(static_cast<int>(c & 1));
     if (next) make_a();
