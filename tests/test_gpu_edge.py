@@ -35,6 +35,10 @@ CASES = [
     (2, 64, 96, 128, "bf16", True, True, 12),       # single-column-block tile, full width
     (2, 60, 72, 129, "f32", True, False, 3),        # two-block tile, second tile mostly idle
     (5, 20, 40, 3, "f32", True, False, 1),          # 32-row tile, out 3
+    # 17..32 rows on wide layers: 8-wave workgroups over 256 columns
+    (3, 32, 200, 300, "f32", True, False, 5),       # second 256-column tile mostly idle, k tail
+    (2, 17, 1000, 129, "bf16", True, False, 2**20), # one row past a 16-row tile, k tail
+    (3, 24, 64, 257, "f32", False, True, 2**35),    # shared x, one column past a 256 tile
     # one or two fp32 rows: the vector-ALU kernel
     (3, 2, 100, 70, "f32", True, False, 4),         # k tail within a chunk, ragged columns
     (2, 2, 1024, 513, "f32", False, True, 2**36),   # shared x, one column past a tile
