@@ -156,9 +156,9 @@ __global__ __launch_bounds__(kThreads) void p_hash_plain(uint32_t* out, uint64_t
 // Noise elements as every kernel consumes them: Weyl-stepped states, N * 2^24
 // as fp32 (centered_q and the conversion), each folded into an fp32
 // accumulator by one fma (eight independent accumulators per lane).
+template <int S>
 __global__ __launch_bounds__(kThreads) void p_noise(uint32_t* out, uint64_t* clk, int iters, uint32_t seed) {
   CLOCK_BEGIN
-  constexpr int S = 8;
   uint64_t z[S];
   float acc[S];
   const uint64_t g = blockIdx.x * kThreads + threadIdx.x;
@@ -296,7 +296,7 @@ int main(int argc, char** argv) {
       {"v_lshl_add_u64", p_add64, kChains, "64-bit"},
       {"hash", p_hash, 8, "hash"},
       {"hash_plain", p_hash_plain, 8, "hash"},
-      {"noise_fma", p_noise, 8, "hash"},
+      {"noise_fma", p_noise<8>, 8, "hash"},
   };
   const double peak_lane_ops = static_cast<double>(cus) * 64.0 * clock_khz * 1e3;
   for (const Probe& pr : probes) {
@@ -335,6 +335,39 @@ int main(int argc, char** argv) {
     std::fflush(stdout);
   }
   // co-execution: 2 waves per SIMD, cycles per slot = SIMD cycles / (slots per wave * waves per SIMD)
+  // The noise sequence at lower occupancy (waves per SIMD) and fewer
+  // independent chains per lane, as the kernels run it: the per-element cost
+  // in lane-cycles at the launch's clock.
+  {
+    struct NoiseCfg {
+      int chains, waves;
+      void (*fn)(uint32_t*, uint64_t*, int, uint32_t);
+    };
+    const NoiseCfg nc[] = {{1, 2, p_noise<1>}, {4, 2, p_noise<4>}, {1, 4, p_noise<1>}, {4, 4, p_noise<4>},
+                           {1, 8, p_noise<1>}, {4, 8, p_noise<4>}};
+    for (const NoiseCfg& c : nc) {
+      const int nb = cus * c.waves;               // blocks of 4 waves: c.waves waves per SIMD
+      const int it = iters * 64 / (c.chains * c.waves);   // the same work per SIMD in every configuration
+      c.fn<<<nb, kThreads>>>(out, clk, it / 8, 1u);
+      CHECK(hipGetLastError());
+      CHECK(hipDeviceSynchronize());
+      CHECK(hipEventRecord(e0));
+      c.fn<<<nb, kThreads>>>(out, clk, it, 2u);
+      CHECK(hipEventRecord(e1));
+      CHECK(hipEventSynchronize(e1));
+      float ms = 0;
+      CHECK(hipEventElapsedTime(&ms, e0, e1));
+      uint64_t cc[2];
+      CHECK(hipMemcpy(cc, clk, sizeof(cc), hipMemcpyDeviceToHost));
+      const double ghz = cc[1] > 0 ? static_cast<double>(cc[0]) / (static_cast<double>(cc[1]) / 100e6) / 1e9 : 0.0;
+      const double elems = static_cast<double>(nb) * kThreads * it * c.chains;
+      const double rate = elems / (ms * 1e-3);
+      std::printf("{\"noise_fma_occupancy\": {\"chains\": %d, \"waves_per_simd\": %d}, \"ms\": %.4f, "
+                  "\"shader_ghz\": %.3f, \"lane_cycles_per_elem_at_that_clock\": %.2f}\n",
+                  c.chains, c.waves, ms, ghz, static_cast<double>(cus) * 64.0 * ghz * 1e9 / rate);
+      std::fflush(stdout);
+    }
+  }
   const CoProbe co[] = {
       {"none", p_coexec<0, 16>, 16},           {"v_mfma_f32_32x32x2_f32", p_coexec<1, 0>, 0},
       {"v_mfma_f32_32x32x2_f32", p_coexec<1, 16>, 16}, {"v_mfma_f32_16x16x4_f32", p_coexec<2, 0>, 0},
