@@ -56,12 +56,22 @@ DEVICE_SRC = os.path.join(ROOT, "virtual_noise_perturbed_amd", "csrc", "vn_devic
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def code_without_comments(text: str) -> str:
+    """C++ source with // and /* */ comments and blank lines removed, so that
+    only code changes count as changes of a kernel (string literals in the
+    kernel sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
     for f in (KERNEL_SRC, DEVICE_SRC):
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(code_without_comments(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -24,13 +24,20 @@
 //  * Forward, larger batches (forward_rows_kernel): the waves split 512 rows
 //    and share one LDS tile of W + sigma*N per k-chunk, so the noise is
 //    generated once per 512 rows.
+//  * Forward, 1-4 fp32 rows (forward_vec_kernel): products on the vector ALUs
+//    in fp32; groups of 16 lanes split k and own columns in turn.
 //  * Forward, fp32 matrix cores (forward_kernel): the same ownership with X
 //    read straight from memory in the A layout; exact fp32 products.
+//  * Layer chain (forward_chain_kernel): every layer of an MLP in one launch,
+//    one workgroup per individual, activations kept in LDS.
 //  * Gradients: element-major (lanes own consecutive elements, the population is
 //    walked with wave-uniform scalar loads of seed and fitness, split over the 4
 //    waves and reduced through LDS in a fixed order) for large blocks;
 //    population-major (lanes own individuals, one wave per element, fixed
 //    butterfly reduction) for small blocks such as biases.
+//  * Reduce metric (metric_kernel): one workgroup per (individual, segment),
+//    runs of four centre values per thread, fixed-order sums; noise readout
+//    (noise_kernel) for verification.
 //  * No atomics anywhere: every output is a fixed-order reduction, so repeated
 //    calls are bit-identical.
 //  * Workgroup ids are remapped so that consecutive logical tiles (the column
