@@ -150,6 +150,7 @@ def virtual_perturbed_linear(x: torch.Tensor, weight: torch.Tensor, bias: Option
     if out is None:
         y = torch.empty((pop, batch, out_f), dtype=torch.float32, device=dev)
     else:
+        _require_device("out", out, dev)
         if out.shape != (pop, batch, out_f) or out.dtype != torch.float32 or not out.is_contiguous():
             raise ValueError("out must be a contiguous float32 (pop, batch, out) tensor")
         y = out
@@ -224,6 +225,7 @@ def virtual_perturbed_mlp(x: torch.Tensor, weights: Sequence[torch.Tensor],
     if out is None:
         y = torch.empty((pop, batch, dims[-1]), dtype=torch.float32, device=dev)
     else:
+        _require_device("out", out, dev)
         if out.shape != (pop, batch, dims[-1]) or out.dtype != torch.float32 or not out.is_contiguous():
             raise ValueError("out must be a contiguous float32 (pop, batch, out_last) tensor")
         y = out
@@ -289,6 +291,7 @@ def virtual_flat_gradient(fitness: torch.Tensor, seeds: torch.Tensor, n: int, si
     if out is None:
         g = torch.empty((int(n),), dtype=torch.float32, device=dev)
     else:
+        _require_device("out", out, dev)
         if out.numel() != int(n) or out.dtype != torch.float32 or not out.is_contiguous():
             raise ValueError("out must be a contiguous float32 tensor with n elements")
         g = out
