@@ -43,16 +43,26 @@ __device__ __forceinline__ uint64_t mul_gamma(uint64_t t) {
   return static_cast<uint64_t>(lo) * kGammaLo + (static_cast<uint64_t>(cross) << 32);
 }
 
-// Finalizer rounds on the state, up to the last product (still 64-bit).
-__device__ __forceinline__ uint64_t mix_rounds(uint64_t z) {
-  z = mul_gamma(z ^ (z >> 30));
-  z = mul_gamma(z ^ (z >> 27));
+// The finalizer in its steps, so that a kernel can run the steps of several
+// elements in lockstep and place other work between them:
+//   round 1 = mul_gamma(xorshift(z, 30)), round 2 = mul_gamma(xorshift(z, 27)),
+//   then keep_words() and, on the 64-bit result, final_centered().
+__device__ __forceinline__ uint64_t xorshift(uint64_t z, int s) { return z ^ (z >> s); }
+
+// Use the product's words as computed: without this the compiler recomputes
+// the low word of the last product with a separate multiply.
+__device__ __forceinline__ uint64_t keep_words(uint64_t z) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  // Use the product's words as computed: without this the compiler
-  // recomputes the low word with a separate multiply.
   asm("" : "+v"(z));
 #endif
   return z;
+}
+
+// Finalizer rounds on the state, up to the last product (still 64-bit).
+__device__ __forceinline__ uint64_t mix_rounds(uint64_t z) {
+  z = mul_gamma(xorshift(z, 30));
+  z = mul_gamma(xorshift(z, 27));
+  return keep_words(z);
 }
 
 // 64-bit state -> low 32 bits of the finalizer output.
@@ -61,12 +71,12 @@ __device__ __forceinline__ uint32_t mix_lo32(uint64_t z) {
   return static_cast<uint32_t>(z ^ (z >> 31));
 }
 
-// 64-bit state -> (r >> 8) - 2^23 as a signed integer, r the finalizer
-// output: the noise times 2^24, exact in fp32.  Flipping bit 31 of r turns
-// the unsigned shift into an arithmetic one on the centred value; the flip
-// rides on the final xor as a three-way xor (one bitop3, at the xor's rate).
-__device__ __forceinline__ int32_t centered_q(uint64_t z) {
-  z = mix_rounds(z);
+// Last step on the output z of mix_rounds: (r >> 8) - 2^23 as a signed
+// integer, r = low word of z ^ (z >> 31): the noise times 2^24, exact in fp32.
+// Flipping bit 31 of r turns the unsigned shift into an arithmetic one on the
+// centred value; the flip rides on the final xor as a three-way xor (one
+// bitop3, at the xor's rate).
+__device__ __forceinline__ int32_t final_centered(uint64_t z) {
   const uint32_t lo = static_cast<uint32_t>(z), hi = static_cast<uint32_t>(z >> 32);
   const uint32_t sh = __builtin_amdgcn_alignbit(hi, lo, 31);   // low word of z >> 31
   uint32_t r;
@@ -77,6 +87,9 @@ __device__ __forceinline__ int32_t centered_q(uint64_t z) {
 #endif
   return static_cast<int32_t>(r) >> 8;
 }
+
+// 64-bit state -> the noise times 2^24 as a signed integer (see final_centered).
+__device__ __forceinline__ int32_t centered_q(uint64_t z) { return final_centered(mix_rounds(z)); }
 
 // Initial state of element `idx` (absolute flat index) for seed `s`.
 __device__ __forceinline__ uint64_t state_of(uint64_t s, uint64_t idx) {

@@ -688,8 +688,6 @@ __global__ __launch_bounds__(512, 1) void forward_rows_kernel(FwdParams p, int64
   constexpr int PLANE = NT * STRIDE;
   constexpr int BUF = PLANES * PLANE;
   constexpr uint64_t kChunkStep = gamma_times(KC);
-  constexpr int kMfmaPerChunk = T * MBW * NB * (SPLIT ? 3 : 1);
-  constexpr int kValuPerMfma = (RB * 24 + T * MBW * 8 * (SPLIT ? 3 : 0)) / kMfmaPerChunk + 1;
   static_assert(GPC == 4 && (RB == 4 || RB % 8 == 0), "tile generation mapping");
 
   __shared__ __attribute__((aligned(16))) __bf16 lds[2 * BUF];
@@ -773,13 +771,8 @@ __global__ __launch_bounds__(512, 1) void forward_rows_kernel(FwdParams p, int64
           load_run_guarded<IN_T, 8>(xr[mb][t], xrow[mb] + k0 + t * 16, static_cast<int>(in - k0 - t * 16 - lh * 8));
       }
   };
-  // W + sigma N of the thread's run -> LDS buffer `buf` (hi, and lo when split).
-  auto make_tile = [&](int buf) {
-    float v[RB];
-#pragma unroll
-    for (int t = 0; t < RB; ++t)
-      v[t] = __builtin_fmaf(p.sigma_q, static_cast<float>(centered_q(z + gamma_times(t))), to_f32(wv[t]));
-    z += kChunkStep;
+  // The thread's run of W + sigma N -> LDS buffer `buf` (hi, and lo when split).
+  auto store_tile = [&](int buf, const float (&v)[RB]) {
     uint32_t hw[RB / 2], lw[RB / 2];
 #pragma unroll
     for (int e = 0; e < RB / 2; ++e) {
@@ -799,6 +792,14 @@ __global__ __launch_bounds__(512, 1) void forward_rows_kernel(FwdParams p, int64
         *reinterpret_cast<Packed*>(&lds[buf * BUF + PLANE + gdst + q * sizeof(Packed) / 2]) = l2;
       }
     }
+  };
+  auto make_tile = [&](int buf) {
+    float v[RB];
+#pragma unroll
+    for (int t = 0; t < RB; ++t)
+      v[t] = __builtin_fmaf(p.sigma_q, static_cast<float>(centered_q(z + gamma_times(t))), to_f32(wv[t]));
+    z += kChunkStep;
+    store_tile(buf, v);
   };
   // X of the loaded chunk -> packed A fragments (hi, and lo when split);
   // bf16 operands are the fragments as loaded.
@@ -849,12 +850,62 @@ __global__ __launch_bounds__(512, 1) void forward_rows_kernel(FwdParams p, int64
       }
   };
 
+  // bf16 operands: the B fragments of a chunk are read right after the barrier
+  // that publishes its tile (their latency hides behind the hash), and the
+  // tile of the next chunk is built with the MFMAs of this one placed among
+  // its steps.  The hash of the thread's RB elements advances in five
+  // lockstep steps (RB independent chains each); each step shares its
+  // scheduling region with a fifth of the MFMAs, which the scheduler spreads
+  // one per ten vector instructions, so that the matrix cores run while the
+  // wave keeps issuing the hash.  (fp32 operands double the B fragments and
+  // would spill; they keep the plain order.)
+  bf16x8 bfh[T][NB];
+  auto read_b = [&](int buf) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        bfh[t][nb] = *reinterpret_cast<const bf16x8*>(&lds[buf * BUF + (nb * 32 + ln) * STRIDE + t * 16 + lh * 8]);
+  };
+  auto tile_and_multiply = [&](int tbuf) {
+    constexpr int NM = T * NB * MBW;
+    constexpr int NST = 5;
+    uint64_t zz[RB];
+    float v[RB];
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+#pragma unroll
+      for (int e = 0; e < RB; ++e) {
+        if (st == 0) zz[e] = xorshift(z + gamma_times(e), 30);
+        if (st == 1) zz[e] = mul_gamma(zz[e]);
+        if (st == 2) zz[e] = xorshift(zz[e], 27);
+        if (st == 3) zz[e] = keep_words(mul_gamma(zz[e]));
+        if (st == 4) v[e] = __builtin_fmaf(p.sigma_q, static_cast<float>(final_centered(zz[e])), to_f32(wv[e]));
+      }
+#pragma unroll
+      for (int m = st * NM / NST; m < (st + 1) * NM / NST; ++m) {
+        const int mb = m % MBW, nb = (m / MBW) % NB, t = m / (MBW * NB);
+        const bf16x8 a_h = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ah[mb][t]));
+        acc[mb][nb] = mfma_bf16<32>(a_h, bfh[t][nb], acc[mb][nb]);
+      }
+#pragma unroll
+      for (int m = st * NM / NST; m < (st + 1) * NM / NST; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    z += kChunkStep;
+    store_tile(tbuf, v);
+  };
+
   // Software pipeline: iteration c loads X of chunk c+1, builds the tile of
   // chunk c+1 in the other LDS buffer from the W run loaded one iteration
   // earlier and loads the W run of chunk c+2, while the matrix cores work on
   // chunk c; then it packs the X of chunk c+1 into the A fragments.  One
   // barrier per iteration.  (Loading W in the same iteration as its tile left
-  // every tile build waiting on a global load.)
+  // every tile build waiting on a global load.)  bf16 operands take the
+  // interleaved step above in the steady state.
   if (nchunks > 0) {
     load_w(0, nfull == 0);
     load_x(0, nfull == 0);
@@ -865,16 +916,19 @@ __global__ __launch_bounds__(512, 1) void forward_rows_kernel(FwdParams p, int64
   __syncthreads();
   int64_t c = 0;
   for (; c + 2 < nfull; ++c) {
-    load_x(c + 1, false);
-    make_tile(static_cast<int>((c + 1) & 1));
-    load_w(c + 2, false);
-    if (live) {
-      multiply(static_cast<int>(c & 1));
-#pragma unroll
-      for (int k = 0; k < kMfmaPerChunk; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
-      }
+    if constexpr (!SPLIT) {
+      // (a wave whose rows all lie past the batch multiplies clamped rows here
+      // and discards the result: keeping the MFMAs unconditional keeps them in
+      // the hash's scheduling regions)
+      read_b(static_cast<int>(c & 1));
+      load_x(c + 1, false);
+      tile_and_multiply(static_cast<int>((c + 1) & 1));
+      load_w(c + 2, false);
+    } else {
+      load_x(c + 1, false);
+      make_tile(static_cast<int>((c + 1) & 1));
+      load_w(c + 2, false);
+      if (live) multiply(static_cast<int>(c & 1));
     }
     make_a();
     __syncthreads();
