@@ -52,6 +52,7 @@ CASES = [
     (1, 513, 16, 128, "f32", False, False, 0),      # one k-chunk, one row past a tile
     (2, 700, 17, 5, "f32", True, False, 8),         # in not a multiple of 4: element loads
     (2, 300, 1000, 260, "bf16", False, True, 5),    # dead waves in the row tile
+    (2, 520, 300, 100, "bf16", True, False, 17),    # own x; 7 of 8 waves past the batch in tile 2
 ]
 
 
