@@ -669,7 +669,10 @@ static hipError_t launch_mm_cfg(const FwdParams& p, hipStream_t stream) {
 // lo planes for fp32 operands) into a double-buffered LDS tile; every wave
 // multiplies its own X rows, read straight from memory in the A layout,
 // against the whole tile.  Each noise element is generated once per 512 rows,
-// so past a few hundred rows the matrix cores, not the hash, bound the kernel.
+// so past a few hundred rows the hash no longer binds: the tile takes
+// (1/128 + 1/512) bytes of X and W per flop from L2, and the rate at which a
+// compute unit can fetch them (its L1 keeps about 60 requests in flight)
+// holds the matrix cores near a third of their peak.
 template <typename IN_T, bool SPLIT, int KC, bool VEC>
 __global__ __launch_bounds__(512, 1) void forward_rows_kernel(FwdParams p, int64_t n_tiles) {
   using MF = Mfma<__bf16, 32>;
