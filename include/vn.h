@@ -36,7 +36,9 @@
  *  - Arrays are dense and row-major.  Floating point inputs are fp32 unless a
  *    vn_dtype argument says otherwise; outputs are fp32.
  *  - Results are deterministic: the same inputs give bit-identical outputs on
- *    every call (no atomics; all reductions run in a fixed order).
+ *    every call (no atomics; all reductions run in a fixed order), except that
+ *    vn_reduce_metric sums in another order when its temporary buffer cannot
+ *    be allocated (see there).
  *  - Calls that write overlapping outputs on the same device must be ordered
  *    by the caller (same stream or events).
  */
@@ -217,7 +219,9 @@ int vn_flat_gradient(const float* fitness, const void* seeds, int32_t seed_dtype
  * partial sums go to a temporary buffer taken from the device's stream-ordered
  * allocator on `stream` and returned on it (pop * segments * 4 bytes, at most
  * 6 KiB); if that allocation fails the call proceeds with one workgroup per
- * individual.  Every sum has a fixed order: repeated calls are bit-identical.
+ * individual, whose sums run in another order (the same means up to fp32
+ * rounding).  Every sum has a fixed order: repeated calls that get the buffer
+ * (or that need none: pop >= 768 or n_params < 131072) are bit-identical.
  */
 int vn_reduce_metric(const float* center, const void* seeds, int32_t seed_dtype, int64_t pop,
                      int64_t n_params, float sigma, int64_t offset, float* out, void* stream);

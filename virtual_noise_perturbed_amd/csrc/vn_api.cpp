@@ -290,8 +290,9 @@ int vn_reduce_metric(const float* center, const void* seeds, int32_t seed_dtype,
   hipStream_t s = static_cast<hipStream_t>(stream);
   // A population too small to fill the GPU with one workgroup per individual
   // splits each individual into segments; their partial sums live in a
-  // stream-ordered temporary buffer.  Without it (allocation failed) the
-  // result is the same, computed with one workgroup per individual.
+  // stream-ordered temporary buffer.  Without it (allocation failed) one
+  // workgroup per individual computes the same means, summed in another order
+  // (equal up to fp32 rounding).
   const int64_t ws = vn::reduce_metric_workspace_floats(pop, n_params);
   float* work = nullptr;
   if (ws > 0 && hipMallocAsync(reinterpret_cast<void**>(&work), static_cast<size_t>(ws) * sizeof(float), s) != hipSuccess) {
