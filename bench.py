@@ -49,6 +49,7 @@ CLOCK_HZ = 2.4e9
 NOISE_LANE_CYCLES = 16.96   # per element per CU lane, at the measured clock (vn_probe noise_fma)
 HASH_PEAK_PER_S = 256 * 64 * CLOCK_HZ / NOISE_LANE_CYCLES
 HBM_PEAK_GBS = 8000.0
+HBM_PEAK = HBM_PEAK_GBS * 1e9   # bytes/s
 MFMA_BF16_PEAK = 2.5e15    # dense bf16 matrix-core FLOP/s
 
 KERNEL_SRC = os.path.join(ROOT, "virtual_noise_perturbed_amd", "csrc", "vn_kernels.hip")
@@ -279,6 +280,26 @@ def fwd_hashes(wl) -> float:
                      for L in wl.layers))
 
 
+def algorithmic_bytes(wl, dom: str, chain_layers, flat_n: int) -> int:
+    """Bytes one launch of `dom` must move at least: every input read once and
+    every output written once (X, W, biases, seeds and Y for a forward; the
+    fitness, the seeds and the gradient for the flat gradient)."""
+    esz = 2 if wl.dtype == "bf16" else 4
+    seeds = wl.pop * 8
+    if dom.startswith("grad"):
+        return wl.pop * 4 + seeds + flat_n * 4
+    layers = chain_layers if dom == "forward_chain" else [wl.layers[int(dom[-1])]]
+    first = layers[0]
+    if dom == "forward_chain" or dom == "forward0":
+        x = (wl.x.size if wl.x.ndim == 2 else wl.pop * wl.batch * first.in_features) * esz
+    else:
+        x = wl.pop * wl.batch * first.in_features * 4      # fp32 activations of the previous layer
+    w = sum(L.out_features * L.in_features * esz + (L.out_features * 4 if L.bias is not None else 0)
+            for L in layers)
+    y = wl.pop * wl.batch * layers[-1].out_features * 4
+    return int(x + w + seeds + y)
+
+
 def grad_elems(wl) -> float:
     return float(sum(wl.pop * (L.out_features * L.in_features + (L.out_features if L.bias is not None else 0))
                      for L in wl.layers))
@@ -425,6 +446,18 @@ def main():
             (1 if wl.dtype == "bf16" else 3)
     t_hash = units / HASH_PEAK_PER_S
     t_mfma = mfma_work / MFMA_BF16_PEAK
+    # The three bounds of the dominant launch as fractions of its measured
+    # duration (the binding one is `frac`): noise generation, matrix cores, and
+    # HBM on its algorithmic bytes (and on the measured traffic when recorded).
+    t_launch = avg_ms[dom] * 1e-3
+    alg_bytes = algorithmic_bytes(wl, dom, chain_layers, step.flat_n)
+    fractions = {
+        "hash": round(t_hash / t_launch, 4),
+        "mfma": round(t_mfma / t_launch, 4),
+        "hbm_algorithmic": round(alg_bytes / HBM_PEAK / t_launch, 4),
+        "hbm_measured": None if traffic is None else round(traffic / HBM_PEAK / t_launch, 4),
+        "algorithmic_bytes_per_launch": alg_bytes,
+    }
     if t_mfma > t_hash:
         roofline = {
             "bound": "mfma",
@@ -438,6 +471,7 @@ def main():
             "avg_launch_ms": round(avg_ms[dom], 4),
             "peak_basis": "dense bf16 matrix cores 2.5 PFLOP/s (fp32 operands count their three bf16 products)",
             "hash_frac": round(achieved / HASH_PEAK_PER_S, 4),
+            "fractions": fractions,
         }
     else:
         roofline = {
@@ -453,6 +487,7 @@ def main():
             "peak_basis": (f"noise generation bound: {NOISE_LANE_CYCLES} lane-cycles per noise element "
                            f"(state step, hash, N as fp32, one fma; measured per shader-clock cycle), "
                            f"256 CUs x 64 lanes x 2.4 GHz"),
+            "fractions": fractions,
         }
 
     value = flops_of(wl) / (ms_per_step * 1e-3) / 1e12
