@@ -39,6 +39,8 @@ CASES = [
     (3, 32, 200, 300, "f32", True, False, 5),       # second 256-column tile mostly idle, k tail
     (2, 17, 1000, 129, "bf16", True, False, 2**20), # one row past a 16-row tile, k tail
     (3, 24, 64, 257, "f32", False, True, 2**35),    # shared x, one column past a 256 tile
+    (11, 32, 64, 1100, "f32", True, False, 3),      # 5 column tiles, 11 individuals: a last group of 3
+    (9, 60, 40, 700, "bf16", False, False, 1),      # 3 column tiles, 9 individuals: a last group of 1
     # one or two fp32 rows: the vector-ALU kernel
     (3, 2, 100, 70, "f32", True, False, 4),         # k tail within a chunk, ragged columns
     (2, 2, 1024, 513, "f32", False, True, 2**36),   # shared x, one column past a tile

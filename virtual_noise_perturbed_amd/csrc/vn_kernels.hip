@@ -65,6 +65,26 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t n) {
   return (x < rem) ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
 }
 
+// (individual, column tile) of workgroup b when every individual has its own
+// X and several column tiles: the tiles of individual i go to blocks 8 apart
+// -- one XCD, one after another in its dispatch order -- and groups of 8
+// consecutive individuals run on the 8 XCDs side by side.  A last group of
+// r < 8 individuals spaces its tiles r apart.  A bijection on
+// [0, pop * n_tiles).  (Against xcd_remap, which gives each XCD a contiguous
+// range of individuals, this order fetched 19% fewer bytes from beyond L2 on a
+// 1024-wide layer with 4 tiles per individual, in the same time; with one tile
+// per individual it reduces to the identity, which ran 3-5% slower than
+// xcd_remap, so it is used only with several tiles.)
+__device__ __forceinline__ void individual_major_order(int64_t b, int64_t pop, int64_t n_tiles, int64_t& i,
+                                                       int64_t& tile) {
+  const int64_t group = b / (kXcds * n_tiles);
+  const int64_t rem = b - group * kXcds * n_tiles;
+  const int64_t left = pop - group * kXcds;
+  const int64_t r = left < kXcds ? left : kXcds;   // individuals in this group
+  tile = rem / r;
+  i = group * kXcds + (rem - tile * r);
+}
+
 // ---------------------------------------------------------------------------
 // MFMA shapes.  For every shape below the A operand of lane l holds row
 // (l % DIM) and the B operand holds column (l % DIM), both at the same k-slots
@@ -350,9 +370,14 @@ __global__ __launch_bounds__(64 * WPG, WAVES) void forward_mm_kernel(FwdParams p
   const int64_t nfull = VEC ? in / KC : 0;            // chunks taken on the unguarded path
   const int64_t nchunks = (in + KC - 1) / KC;
 
-  const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t i = L / n_tiles;
-  const int64_t tile = L - i * n_tiles;
+  int64_t i, tile;
+  if (p.x_pop_stride != 0 && n_tiles > 1) {
+    individual_major_order(blockIdx.x, p.pop, n_tiles, i, tile);
+  } else {
+    const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
+    i = L / n_tiles;
+    tile = L - i * n_tiles;
+  }
   const uint64_t s = load_seed(p.seeds, p.seeds_i32, i);
   const IN_T* __restrict__ xi = static_cast<const IN_T*>(p.x) + i * p.x_pop_stride;
   const IN_T* __restrict__ w = static_cast<const IN_T*>(p.w);
