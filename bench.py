@@ -529,6 +529,25 @@ def main():
                                 "from events inside the timed region"),
         },
     }
+    # side measurement: the dominant launch with cold caches -- a 512 MiB
+    # buffer (more than L2 and Infinity Cache together) is written before each
+    # repetition, outside the launch's event pair
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=device)
+    dom_fn = dict(step.forward_launches() + step.gradient_launches())[dom]
+    reps = min(args.steps, 20)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for r, (a, b) in enumerate(pairs):
+        flush.fill_(float(r))
+        a.record()
+        dom_fn()
+        b.record()
+    torch.cuda.synchronize()
+    cold_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+    del flush
+    result["breakdown"]["dominant_cold_cache_ms"] = round(cold_ms, 4)
+    result["breakdown"]["dominant_cold_cache_note"] = (
+        f"{dom}, mean of {reps} launches each after a 512 MiB write; the timed steps run warm, "
+        f"back to back")
     if wl.dtype == "f32":
         # side measurement: the same forward on the fp32 matrix cores (math mode "f32")
         for _ in range(2):
