@@ -143,3 +143,65 @@ def test_planted_gradient_scale_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(vo, "weight_gradient",
                         lambda f, s, shp, sig, p, off: real(f, s, shp, sig, p, off) * p)
     assert _run_all()
+
+
+def _metric_without_abs(center, seeds, sigma, n_params, offset=0):
+    c = np.asarray(center, dtype=np.float64).reshape(-1)
+    s = vo.canonical_seeds(seeds)
+    return np.array([np.mean(c + sigma * vo.noise(s[i:i + 1].view(np.int64), n_params, offset)[0])
+                     for i in range(s.shape[0])])
+
+
+def _metric_sum_not_mean(center, seeds, sigma, n_params, offset=0):
+    c = np.asarray(center, dtype=np.float64).reshape(-1)
+    s = vo.canonical_seeds(seeds)
+    return np.array([np.sum(np.abs(c + sigma * vo.noise(s[i:i + 1].view(np.int64), n_params, offset)[0]))
+                     for i in range(s.shape[0])])
+
+
+def _metric_offset_ignored(center, seeds, sigma, n_params, offset=0):
+    c = np.asarray(center, dtype=np.float64).reshape(-1)
+    s = vo.canonical_seeds(seeds)
+    return np.array([np.mean(np.abs(c + sigma * vo.noise(s[i:i + 1].view(np.int64), n_params, 0)[0]))
+                     for i in range(s.shape[0])])
+
+
+def _bias_gradient_forward_offsets(fitness, seeds, bias_shape, sigma, pop_size, offset):
+    # mistake: `offset` treated as a weight offset and moved past a weight block (here one of
+    # out x out elements) before the bias noise is read, where the bias gradient takes the
+    # bias-region offset itself
+    (out_f,) = bias_shape
+    f = np.asarray(fitness, dtype=np.float64)
+    n = vo.noise_at(seeds, offset + out_f * out_f + np.arange(out_f))
+    return (f @ n) / (pop_size * sigma)
+
+
+def _weight_gradient_transposed(fitness, seeds, weight_shape, sigma, pop_size, offset):
+    out_f, in_f = weight_shape
+    f = np.asarray(fitness, dtype=np.float64)
+    n = vo.noise_at(seeds, offset + np.arange(out_f * in_f))
+    return ((f @ n) / (pop_size * sigma)).reshape(in_f, out_f).T.copy()
+
+
+def _offsets_inclusive(param_shapes):
+    out, acc = [], 0
+    for shp in param_shapes:
+        acc += int(np.prod(shp)) if len(shp) else 1
+        out.append(acc)
+    return out
+
+
+MORE_MUTATIONS = [
+    ("reduce_metric", _metric_without_abs),
+    ("reduce_metric", _metric_sum_not_mean),
+    ("reduce_metric", _metric_offset_ignored),
+    ("bias_gradient", _bias_gradient_forward_offsets),
+    ("weight_gradient", _weight_gradient_transposed),
+    ("compute_offsets", _offsets_inclusive),
+]
+
+
+@pytest.mark.parametrize("name,fn", MORE_MUTATIONS, ids=[f"{n}:{f.__name__}" for n, f in MORE_MUTATIONS])
+def test_planted_api_mistake_is_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(vo, name, fn)
+    assert _run_all(), f"no pin caught the planted mistake {fn.__name__}"
