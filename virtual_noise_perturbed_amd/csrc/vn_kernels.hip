@@ -1376,14 +1376,14 @@ __global__ __launch_bounds__(512, 4) void forward_chain_kernel(ChainParams p) {
       }
       __syncthreads();
       if (live && q == 0) {
+        // the other waves' sums in wave order, all values of one wave at a
+        // time so that their LDS reads overlap (acc holds this wave's own)
+        for (int u = 1; u < wpb; ++u) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+          for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int v = 0; v < MF::NACC; ++v) {
-            float t = part[((wave * MB + mb) * MF::NACC + v) * 64 + lane];
-            for (int u = 1; u < wpb; ++u) t += part[(((wave + u) * MB + mb) * MF::NACC + v) * 64 + lane];
-            acc[mb][v] = t;
-          }
+            for (int v = 0; v < MF::NACC; ++v) acc[mb][v] += part[(((wave + u) * MB + mb) * MF::NACC + v) * 64 + lane];
+        }
       }
       __syncthreads();                         // partial sums consumed
     }
