@@ -1375,20 +1375,25 @@ __global__ __launch_bounds__(512, 4) void forward_chain_kernel(ChainParams p) {
           for (int v = 0; v < MF::NACC; ++v) part[((wave * MB + mb) * MF::NACC + v) * 64 + lane] = acc[mb][v];
       }
       __syncthreads();
-      if (live && q == 0) {
-        // the other waves' sums in wave order, all values of one wave at a
-        // time so that their LDS reads overlap (acc holds this wave's own)
-        for (int u = 1; u < wpb; ++u) {
+      if (live) {
+        // value e = mb * NACC + v of the block belongs to its wave e % wpb,
+        // which adds the block's partial sums in wave order (the waves share
+        // the additions and the stores below)
+        const int w0 = wave - q;
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int v = 0; v < MF::NACC; ++v) acc[mb][v] += part[(((wave + u) * MB + mb) * MF::NACC + v) * 64 + lane];
-        }
+          for (int v = 0; v < MF::NACC; ++v) {
+            if ((mb * MF::NACC + v) % wpb != q) continue;
+            float t = part[((w0 * MB + mb) * MF::NACC + v) * 64 + lane];
+            for (int u = 1; u < wpb; ++u) t += part[(((w0 + u) * MB + mb) * MF::NACC + v) * 64 + lane];
+            acc[mb][v] = t;
+          }
       }
       __syncthreads();                         // partial sums consumed
     }
 
-    if (live && q == 0) {
+    if (live) {
       const int64_t j = jbase + ln;
       float bj = 0.0f;
       if (p.bias[l] != nullptr && j < out) {
@@ -1404,6 +1409,7 @@ __global__ __launch_bounds__(512, 4) void forward_chain_kernel(ChainParams p) {
       for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int v = 0; v < MF::NACC; ++v) {
+          if ((mb * MF::NACC + v) % wpb != q) continue;   // another wave of the block stores it
           const int row = mb * 32 + rb + MF::row_off(v);
           float val = acc[mb][v] + bj;
           if (last) {
