@@ -45,6 +45,33 @@ CASES = [
 @pytest.mark.parametrize("case", [c for c in CASES if len(c[2]) > 1],
                          ids=[f"{c[3]}-p{c[0]}b{c[1]}-{'x'.join(map(str, c[2]))}" for c in CASES if len(c[2]) > 1])
 def test_chain_matches_oracle(case):
+    _check_chain(case)
+
+
+def _random_chain_cases(n=16, seed=7):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        n_layers = int(rng.integers(2, 5))
+        dims = [int(rng.integers(1, 900))] + [int(rng.integers(1, 257)) for _ in range(n_layers)]
+        out.append((int(rng.integers(1, 9)), int(rng.integers(1, 65)), dims,
+                    "bf16" if rng.random() < 0.4 else "f32", [bool(rng.random() < 0.7) for _ in range(n_layers)],
+                    bool(rng.random() < 0.3), bool(rng.random() < 0.7),
+                    [int(rng.integers(0, 1 << 36)) for _ in range(n_layers)]))
+    return out
+
+
+RANDOM_CASES = _random_chain_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES,
+                         ids=[f"{c[3]}-p{c[0]}b{c[1]}-{'x'.join(map(str, c[2]))}" for c in RANDOM_CASES])
+def test_random_chain_matches_oracle(case):
+    """Seeded random chains: widths, depth, rows, dtype, biases, shared x, ReLU, offsets."""
+    _check_chain(case)
+
+
+def _check_chain(case):
     pop, batch, dims, dt, has_b, shared, relu, offsets = case
     print(f"chain {case}", flush=True)
     rng = np.random.default_rng(sum(dims) + batch)
