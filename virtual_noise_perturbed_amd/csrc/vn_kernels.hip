@@ -40,9 +40,10 @@
 //    (noise_kernel) for verification.
 //  * No atomics anywhere: every output is a fixed-order reduction, so repeated
 //    calls are bit-identical.
-//  * Workgroup ids are remapped so that consecutive logical tiles (the column
-//    tiles of one individual, which share its X rows) land on the same XCD and
-//    its L2, given that the hardware deals workgroups round-robin over 8 XCDs.
+//  * Workgroup ids are remapped with the XCDs in mind (the hardware deals
+//    workgroups round-robin over 8 XCDs, each with its own L2): the column
+//    tiles of one individual, which share its X rows, run one after another
+//    on one XCD (xcd_remap, individual_major_order).
 
 #include <type_traits>
 
