@@ -215,13 +215,13 @@ int vn_flat_gradient(const float* fitness, const void* seeds, int32_t seed_dtype
  * Mean-absolute reduction metric (API entry virtual_reduce_metric):
  *   out[i] = (1/n_params) sum_k | center[k] + sigma noise_i[offset + k] |
  *   center (n_params,) fp32;  out (pop,) fp32;  n_params > 0 when pop > 0.
- * A population below 768 splits each individual's sum into segments whose
+ * A population below 512 splits each individual's sum into segments whose
  * partial sums go to a temporary buffer taken from the device's stream-ordered
  * allocator on `stream` and returned on it (pop * segments * 4 bytes, at most
  * 6 KiB); if that allocation fails the call proceeds with one workgroup per
  * individual, whose sums run in another order (the same means up to fp32
  * rounding).  Every sum has a fixed order: repeated calls that get the buffer
- * (or that need none: pop >= 768 or n_params < 131072) are bit-identical.
+ * (or that need none: pop >= 512 or n_params < 131072) are bit-identical.
  */
 int vn_reduce_metric(const float* center, const void* seeds, int32_t seed_dtype, int64_t pop,
                      int64_t n_params, float sigma, int64_t offset, float* out, void* stream);

@@ -145,7 +145,12 @@ def test_degenerate_sizes():
     assert_close(g, oracle.weight_gradient_at(np.array([2.0]), np.array([0]), 0.25, 1, 123, [0]), TOL_F32, "1x1")
 
 
-@pytest.mark.parametrize("pop,n", [(1, 5), (63, 1000), (64, 16384), (65, 16385), (1000, 3000), (3, 70001)])
+# The last three split the population over 16 waves per workgroup (few
+# workgroups, long parts of the population): one element per lane with a
+# population that 16 does not divide, four per lane, and four per lane at the
+# largest element count that still takes the split.
+@pytest.mark.parametrize("pop,n", [(1, 5), (63, 1000), (64, 16384), (65, 16385), (1000, 3000), (3, 70001),
+                                   (4099, 17385), (1030, 2**20 + 100), (1024, 2**21 - 300)])
 def test_gradient_shapes(pop, n):
     print(f"gradient pop={pop} n={n}", flush=True)
     rng = np.random.default_rng(pop + n)
@@ -169,8 +174,10 @@ def test_binding_checks_pop_size():
 
 @pytest.mark.parametrize("pop,n,offset", [(6, 1000, 0), (3, 269322, 5), (1, 1, 2**35), (40, 4097, 77), (2, 3, 9),
                                           (5, 4096 * 3 + 2, 1), (300, 2051, 13), (1, (1 << 20) + 3, 3),
-                                          (200, 140000, 0)])
+                                          (200, 140000, 0), (511, 131076, 2), (512, 131076, 2)])
 def test_reduce_metric(pop, n, offset):
+    # (511, 131076): the largest population that still splits (two segments);
+    # (512, 131076): the smallest that takes one workgroup per individual
     print(f"reduce metric pop={pop} n={n}", flush=True)
     rng = np.random.default_rng(n)
     center = rng.standard_normal(n).astype(np.float32)

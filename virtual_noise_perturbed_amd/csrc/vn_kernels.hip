@@ -1522,17 +1522,20 @@ hipError_t launch_forward_bf16_exact(const FwdParams& p, hipStream_t stream) {
 
 // ---------------------------------------------------------------------------
 // Gradient, element-major: grad[t] = scale * sum_i f_i noise_i[offset + t].
-// Lane owns E consecutive elements; wave w walks its quarter of the population
-// in groups of four individuals, whose seeds and fitness values (wave-uniform,
-// scalar loads) are fetched one group ahead.  The sums run over the integers
+// A workgroup owns 64*E consecutive elements, lane l of every wave the E at
+// l*E; its S waves split the population into S contiguous parts.  Each wave
+// walks its part in groups of four individuals, whose seeds and fitness values
+// (wave-uniform, scalar loads) are fetched one group ahead.  The S partial sums
+// of an element are added in wave order.  The sums run over the integers
 // N * 2^24 and take the 2^-24 at the end: a power-of-two factor, so every
 // rounding is the one of the sum over N.
-template <int E, bool SEEDS_I32>
-__global__ __launch_bounds__(256) void grad_elem_kernel(GradParams p, int64_t n_blocks) {
-  __shared__ float red[4][64 * E];
+template <int E, bool SEEDS_I32, int S>
+__global__ __launch_bounds__(64 * S) void grad_elem_kernel(GradParams p, int64_t n_blocks) {
+  static_assert(S >= E, "the final sums take one thread per element");
+  __shared__ float red[S][64 * E];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t q = p.pop / 4, r = p.pop % 4;
+  const int64_t q = p.pop / S, r = p.pop % S;
   const int64_t i_begin = wave * q + (wave < r ? wave : r);
   const int64_t i_end = i_begin + q + (wave < r ? 1 : 0);
   // Nothing the kernel writes aliases the inputs: lets the compiler use scalar loads.
@@ -1594,26 +1597,47 @@ __global__ __launch_bounds__(256) void grad_elem_kernel(GradParams p, int64_t n_
 #pragma unroll
     for (int e = 0; e < E; ++e) red[wave][lane * E + e] = acc[e];
     __syncthreads();
-    if (wave == 0) {
+    if (threadIdx.x < 64 * E) {
+      const int k = threadIdx.x;
+      float v = red[0][k];
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int k = lane * E + e;
-        const float v = ((red[0][k] + red[1][k]) + red[2][k]) + red[3][k];
-        if (e0 + e < p.n) out[e0 + e] = (v * 0x1p-24f) * p.scale;
-      }
+      for (int w = 1; w < S; ++w) v += red[w][k];
+      const int64_t t = blk * (64 * E) + k;
+      if (t < p.n) out[t] = (v * 0x1p-24f) * p.scale;
     }
     __syncthreads();
   }
 }
 
+// Waves per workgroup.  Workgroups are handed out in rounds of (CUs x
+// workgroups a CU holds, 8 of 4 waves here); a last, partly filled round leaves
+// most of the chip idle for one workgroup's duration.  With 16 waves a
+// workgroup takes a quarter as long as with 4 for the same work, which shortens
+// that round, but each wave then pays its setup and the final sums over a
+// quarter of the noise.  Measured: 16 waves gain 7% when a wave's part is 1024
+// noise values per lane in 2052 workgroups (population 4096, 512x256 layer),
+// and lose 2-8% when it would be 64-256 values; so 16 only for few workgroups
+// (under four rounds) and when a 4-wave part is at least 1024 values.
+inline int grad_elem_waves(int64_t n_blocks, int64_t pop, int e) {
+  return (n_blocks < 8192 && pop * e >= 4096) ? 16 : 4;
+}
+
+template <int E, int S>
+static void launch_grad_elem_s(const GradParams& p, int64_t n_blocks, hipStream_t stream) {
+  const int64_t g = n_blocks < kMaxGridX ? n_blocks : kMaxGridX;
+  if (p.seeds_i32)
+    grad_elem_kernel<E, true, S><<<static_cast<unsigned>(g), 64 * S, 0, stream>>>(p, n_blocks);
+  else
+    grad_elem_kernel<E, false, S><<<static_cast<unsigned>(g), 64 * S, 0, stream>>>(p, n_blocks);
+}
+
 template <int E>
 static void launch_grad_elem(const GradParams& p, hipStream_t stream) {
   const int64_t n_blocks = (p.n + 64 * E - 1) / (64 * E);
-  const int64_t g = n_blocks < kMaxGridX ? n_blocks : kMaxGridX;
-  if (p.seeds_i32)
-    grad_elem_kernel<E, true><<<static_cast<unsigned>(g), 256, 0, stream>>>(p, n_blocks);
+  if (grad_elem_waves(n_blocks, p.pop, E) == 16)
+    launch_grad_elem_s<E, 16>(p, n_blocks, stream);
   else
-    grad_elem_kernel<E, false><<<static_cast<unsigned>(g), 256, 0, stream>>>(p, n_blocks);
+    launch_grad_elem_s<E, 4>(p, n_blocks, stream);
 }
 
 // Gradient, population-major: one wave per element, lanes own individuals.
@@ -1767,11 +1791,14 @@ __global__ __launch_bounds__(256) void metric_finish(const float* partial, int64
   out[i] = t / static_cast<float>(n);
 }
 
-// Segments per individual: enough workgroups for three per CU (the most that
-// fit: 12 waves per SIMD), segments of at least 64K elements.
+// Segments per individual.  A CU holds two of these 16-wave workgroups (8
+// waves per SIMD), 512 on the chip.  From one such round of individuals on,
+// one segment each is fastest (no finishing launch: 6% on 512 individuals of
+// 269K parameters).  Smaller populations split into segments of at least 64K
+// elements, aiming at two whole rounds (1024 workgroups; 1-3% faster than 1.5).
 static int64_t metric_segments(int64_t pop, int64_t n) {
-  constexpr int64_t kTargetGroups = 768, kMinSeg = 65536;
-  if (pop >= kTargetGroups) return 1;
+  constexpr int64_t kOneRound = 512, kTargetGroups = 1024, kMinSeg = 65536;
+  if (pop >= kOneRound) return 1;
   int64_t seg = (kTargetGroups + pop - 1) / pop;
   const int64_t by_len = n / kMinSeg;
   if (seg > by_len) seg = by_len;
