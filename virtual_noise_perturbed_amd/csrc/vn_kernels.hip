@@ -31,8 +31,9 @@
 //  * Layer chain (forward_chain_kernel): every layer of an MLP in one launch,
 //    one workgroup per individual, activations kept in LDS.
 //  * Gradients: element-major (lanes own consecutive elements, the population is
-//    walked with wave-uniform scalar loads of seed and fitness, split over the 4
-//    waves and reduced through LDS in a fixed order) for large blocks;
+//    walked with wave-uniform scalar loads of seed and fitness, split over the
+//    4 or 16 waves of a workgroup and reduced through LDS in a fixed order) for
+//    large blocks;
 //    population-major (lanes own individuals, one wave per element, fixed
 //    butterfly reduction) for small blocks such as biases.
 //  * Reduce metric (metric_kernel): one workgroup per (individual, segment),
