@@ -548,6 +548,31 @@ def main():
     result["breakdown"]["dominant_cold_cache_note"] = (
         f"{dom}, mean of {reps} launches each after a 512 MiB write; the timed steps run warm, "
         f"back to back")
+    # side measurement: the whole step captured once as a HIP graph and
+    # replayed, so no host work stands between launches (what launch-bound
+    # shapes cost on the device alone); every output is preallocated
+    side = torch.cuda.Stream(device=device)            # default priority
+    side.wait_stream(torch.cuda.current_stream(device))
+    with torch.cuda.stream(side):
+        step.run()
+    torch.cuda.current_stream(device).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step.run()
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    result["breakdown"]["graph_step_ms"] = round(a.elapsed_time(b) / args.steps, 4)
+    result["breakdown"]["graph_step_note"] = (
+        f"the step captured once as a HIP graph, {args.steps} replays back to back; value and ms_per_step "
+        f"are the eager steps")
+    del graph
     if wl.dtype == "f32":
         # side measurement: the same forward on the fp32 matrix cores (math mode "f32")
         for _ in range(2):

@@ -1,0 +1,70 @@
+"""The hot path under HIP graph capture.
+
+Every entry point launches on the caller's current stream and allocates
+nothing when its outputs are given, so a forward and a gradient can be
+captured into one graph.  Replays, with eager work and synchronizations in
+between and a new fitness vector written in place before one of them, must
+give exactly what eager calls give (the same kernels in a fixed order)."""
+
+import numpy as np
+import pytest
+import torch
+
+import virtual_noise_perturbed_amd as vn
+from gpu_util import device
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replays_match_eager():
+    print("graph capture: two-layer forward + flat gradient", flush=True)
+    dev = device()
+    g = torch.Generator().manual_seed(7)
+    pop, batch, d0, d1, d2 = 24, 5, 70, 48, 10
+    x = torch.randn(pop, batch, d0, generator=g).to(dev)
+    w1 = (torch.randn(d1, d0, generator=g) / d0 ** 0.5).to(dev)
+    b1 = torch.randn(d1, generator=g).to(dev)
+    w2 = (torch.randn(d2, d1, generator=g) / d1 ** 0.5).to(dev)
+    seeds = (torch.arange(pop) * 1009 - 5).to(dev)
+    fit = torch.randn(pop, generator=g).to(dev)
+    offs = vn.compute_offsets([(d1, d0), (d1,), (d2, d1)])
+    n = offs[-1] + d2 * d1
+    h = torch.empty(pop, batch, d1, device=dev)
+    y = torch.empty(pop, batch, d2, device=dev)
+    grad = torch.empty(n, device=dev)
+    sigma = 0.05
+
+    def step():
+        vn.virtual_perturbed_linear(x, w1, b1, seeds, sigma, offs[0], activation="relu", out=h)
+        vn.virtual_perturbed_linear(h, w2, None, seeds, sigma, offs[2], out=y)
+        vn.virtual_flat_gradient(fit, seeds, n, sigma, pop, 0, out=grad)
+
+    def eager():
+        step()
+        torch.cuda.synchronize()
+        return h.clone(), y.clone(), grad.clone()
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    want = eager()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    new_fit = torch.randn(pop, generator=g).to(dev)
+    for r in range(4):
+        h.zero_(), y.zero_(), grad.zero_()
+        if r == 2:                              # new inputs, written in place
+            fit.copy_(new_fit)
+            want = eager()
+            h.zero_(), y.zero_(), grad.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _ = (torch.ones(1000, device=dev) * r).sum().item()    # eager work between replays
+        for got, exp, name in zip((h, y, grad), want, ("hidden", "output", "gradient")):
+            assert torch.equal(got, exp), f"replay {r}: {name}"
+    assert not np.array_equal(want[2].cpu().numpy(), np.zeros(n, dtype=np.float32))
