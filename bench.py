@@ -319,10 +319,11 @@ def cpu_baseline(wl, budget_s: float):
     # forward: whole individuals through every layer
     t0 = time.perf_counter()
     k = 0
-    while k < wl.pop and (time.perf_counter() - t0) < budget_s / 2:
-        h = (wl.x[None] if wl.x.ndim == 2 else wl.x[k:k + 1]).astype(np.float64)
+    while k == 0 or (time.perf_counter() - t0) < budget_s / 2:   # individuals in turn, cycling
+        i = k % wl.pop
+        h = (wl.x[None] if wl.x.ndim == 2 else wl.x[i:i + 1]).astype(np.float64)
         for li, L in enumerate(wl.layers):
-            h = oracle.perturbed_linear(h, L.weight, L.bias, wl.seeds[k:k + 1], sig, L.w_offset)
+            h = oracle.perturbed_linear(h, L.weight, L.bias, wl.seeds[i:i + 1], sig, L.w_offset)
             if wl.relu_between and li < len(wl.layers) - 1:
                 h = np.maximum(h, 0.0)
         k += 1
@@ -334,7 +335,7 @@ def cpu_baseline(wl, budget_s: float):
     t1 = time.perf_counter()
     m = 0
     chunk = 4096
-    while m < total and (time.perf_counter() - t1) < budget_s / 2:
+    while m == 0 or (time.perf_counter() - t1) < budget_s / 2:
         start = int(rng.integers(0, max(total - chunk, 1)))
         oracle.weight_gradient_at(fit, wl.seeds, sig, wl.pop, 0, np.arange(start, min(start + chunk, total)))
         m += min(chunk, total)
@@ -348,8 +349,8 @@ def cpu_baseline(wl, budget_s: float):
         "unit": "TFLOP/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"numpy oracle, 1 thread: forward of {k} of {wl.pop} individuals through all layers "
-                   f"({t_fwd:.1f} s) and gradients of {m // min(chunk, total)} runs of {min(chunk, total)} flat "
+        "sample": (f"numpy oracle, 1 thread: forward of {k} individuals (in turn over the population of "
+                   f"{wl.pop}) through all layers ({t_fwd:.1f} s) and gradients of {m // min(chunk, total)} runs of {min(chunk, total)} flat "
                    f"elements at random starts (of {total}) over all {wl.pop} individuals ({t_grad:.1f} s), "
                    f"scaled to one step ({est_step:.1f} s)"),
         "step_s_estimate": est_step,
