@@ -527,7 +527,10 @@ def main():
                                               (fwd_ms * 1e-3) / 2.5e15, 4),
             "per_launch_ms": {k: round(v, 4) for k, v in avg_ms.items()},
             "per_launch_note": ("event-bracketed steps outside the timed region; the dominant launch "
-                                "from events inside the timed region"),
+                                "from events inside the timed region. A bracketed launch also takes the gap "
+                                "between its event records and the kernel (a few us, more after a forward), "
+                                "so the per-launch times add up to more than ms_per_step, whose unbracketed "
+                                "steps are the sum of the kernel times"),
         },
     }
     # side measurement: the dominant launch with cold caches -- a 512 MiB
