@@ -6,10 +6,11 @@ perturbed-linear forward of every layer of the workload, then the weight and
 bias gradient estimators of every parameter block.  Inputs are resident in
 HBM before the timed region.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload 5] [--no-cpu-baseline]
 
-The default workload is the MLP hidden layer (pop 256, batch 32 per
-individual, 1024 -> 1024, fp32).  Per-kernel durations come from HIP events
+The default workload is the largest of the five reference configurations, the
+transformer-width projection (pop 128, batch 256 per individual, 4096 -> 4096,
+bf16 operands with fp32 accumulation).  Per-kernel durations come from HIP events
 recorded on the stream the kernels are launched on, inside the timed steps.
 """
 
@@ -95,7 +96,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate CPU seconds for the oracle baseline sample")
