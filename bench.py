@@ -306,54 +306,102 @@ def grad_elems(wl) -> float:
                      for L in wl.layers))
 
 
-def cpu_baseline(wl, budget_s: float):
-    """Time the CPU oracle (single thread) on a bounded sample of the same
-    workload and scale it to one step of the metric's unit."""
-    import oracle
+_CPU_WL = None
+
+
+def _cpu_worker_init(key: int):
+    """Pool worker: one BLAS thread, the workload built once."""
+    global _CPU_WL
     try:
         from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(1)
+        threadpool_limits(1)
     except Exception:  # pragma: no cover
-        limiter = None
-    sig = float(np.float32(wl.sigma))
-    fit = wl.fitness.astype(np.float64)
-    # forward: whole individuals through every layer
+        pass
+    import workloads
+    _CPU_WL = workloads.make(key)
+
+
+def _cpu_forward_job(i: int) -> float:
+    """The oracle forward of individual i through every layer; seconds taken."""
+    import oracle
+    wl = _CPU_WL
     t0 = time.perf_counter()
-    k = 0
-    while k == 0 or (time.perf_counter() - t0) < budget_s / 2:   # individuals in turn, cycling
-        i = k % wl.pop
-        h = (wl.x[None] if wl.x.ndim == 2 else wl.x[i:i + 1]).astype(np.float64)
-        for li, L in enumerate(wl.layers):
-            h = oracle.perturbed_linear(h, L.weight, L.bias, wl.seeds[i:i + 1], sig, L.w_offset)
-            if wl.relu_between and li < len(wl.layers) - 1:
-                h = np.maximum(h, 0.0)
-        k += 1
-    t_fwd = time.perf_counter() - t0
-    fwd_per_indiv = t_fwd / k
-    # gradients: chunks of flat elements of the chained parameter vector (all individuals)
+    sig = float(np.float32(wl.sigma))
+    h = (wl.x[None] if wl.x.ndim == 2 else wl.x[i:i + 1]).astype(np.float64)
+    for li, L in enumerate(wl.layers):
+        h = oracle.perturbed_linear(h, L.weight, L.bias, wl.seeds[i:i + 1], sig, L.w_offset)
+        if wl.relu_between and li < len(wl.layers) - 1:
+            h = np.maximum(h, 0.0)
+    return time.perf_counter() - t0
+
+
+def _cpu_gradient_job(start_count) -> float:
+    """The oracle gradient estimator over `count` flat elements from `start`, all individuals."""
+    import oracle
+    wl = _CPU_WL
+    start, count = start_count
+    t0 = time.perf_counter()
+    oracle.weight_gradient_at(wl.fitness.astype(np.float64), wl.seeds, float(np.float32(wl.sigma)), wl.pop, 0,
+                              np.arange(start, start + count))
+    return time.perf_counter() - t0
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(wl, budget_s: float, max_procs: int = 16):
+    """Time the CPU oracle on the host's cores on a bounded sample of the same
+    workload and scale it to one step of the metric's unit.  One process per
+    core (at most `max_procs`, the host share of one GPU), each running the
+    oracle with one BLAS thread; half the budget goes to whole individuals
+    through the forward (in turn, cycling over the population), half to runs
+    of 4096 gradient elements at random starts over the full population."""
+    import multiprocessing as mp
+    procs = max(1, min(os.cpu_count() or 1, max_procs))
+    ctx = mp.get_context("spawn")          # the workers never touch the GPU or inherit its state
     rng = np.random.default_rng(0)
     total = wl.total_params
-    t1 = time.perf_counter()
-    m = 0
-    chunk = 4096
-    while m == 0 or (time.perf_counter() - t1) < budget_s / 2:
-        start = int(rng.integers(0, max(total - chunk, 1)))
-        oracle.weight_gradient_at(fit, wl.seeds, sig, wl.pop, 0, np.arange(start, min(start + chunk, total)))
-        m += min(chunk, total)
-    t_grad = time.perf_counter() - t1
+    chunk = min(4096, total)
+    with ctx.Pool(procs, initializer=_cpu_worker_init, initargs=(wl.key,)) as pool:
+        pool.map(_cpu_forward_job, [0] * procs)          # workers built and warm before timing
+        # forward: rounds of `procs` individuals until half the budget is spent
+        t0 = time.perf_counter()
+        k = 0
+        while k == 0 or time.perf_counter() - t0 < budget_s / 2:
+            pool.map(_cpu_forward_job, [(k + q) % wl.pop for q in range(procs)])
+            k += procs
+        t_fwd = time.perf_counter() - t0
+        # gradients: rounds of `procs` runs of `chunk` flat elements
+        t1 = time.perf_counter()
+        m = 0
+        while m == 0 or time.perf_counter() - t1 < budget_s / 2:
+            starts = [int(rng.integers(0, max(total - chunk, 1))) for _ in range(procs)]
+            pool.map(_cpu_gradient_job, [(st, chunk) for st in starts])
+            m += procs * chunk
+        t_grad = time.perf_counter() - t1
+    fwd_per_indiv = t_fwd / k                   # wall seconds per individual with all workers busy
     grad_per_elem = t_grad / m
-    if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
     est_step = fwd_per_indiv * wl.pop + grad_per_elem * total
     return {
         "value": flops_of(wl) / est_step / 1e12,
         "unit": "TFLOP/s",
-        "cores": 1,
+        "cores": procs,
         "kind": "oracle",
-        "sample": (f"numpy oracle, 1 thread: forward of {k} individuals (in turn over the population of "
-                   f"{wl.pop}) through all layers ({t_fwd:.1f} s) and gradients of {m // min(chunk, total)} runs of {min(chunk, total)} flat "
-                   f"elements at random starts (of {total}) over all {wl.pop} individuals ({t_grad:.1f} s), "
-                   f"scaled to one step ({est_step:.1f} s)"),
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
+        "sample": (f"numpy oracle in {procs} processes x 1 BLAS thread: forward of {k} individuals (in turn over "
+                   f"the population of {wl.pop}) through all layers ({t_fwd:.1f} s wall) and gradients of "
+                   f"{m // chunk} runs of {chunk} flat elements at random starts (of {total}) over all "
+                   f"{wl.pop} individuals ({t_grad:.1f} s wall), scaled to one step ({est_step:.2f} s)"),
         "step_s_estimate": est_step,
         "grad_elements_per_s": wl.pop * m / t_grad,
     }

@@ -25,8 +25,9 @@
  *
  * Conventions for every entry point below:
  *  - All pointers except those of vn_compute_offsets are DEVICE pointers owned
- *    by the caller.  The library keeps no state; the only memory it takes is
- *    the small stream-ordered temporary buffer of vn_reduce_metric (see there).
+ *    by the caller.  The library keeps no state and allocates no memory: the
+ *    one entry point that needs scratch space (vn_reduce_metric) takes it from
+ *    the caller.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = null stream).
  *    VN_OK means "validated and enqueued"; outputs are valid once the stream
  *    reaches the launch.  Arguments are validated before any HIP call and a
@@ -36,9 +37,8 @@
  *  - Arrays are dense and row-major.  Floating point inputs are fp32 unless a
  *    vn_dtype argument says otherwise; outputs are fp32.
  *  - Results are deterministic: the same inputs give bit-identical outputs on
- *    every call (no atomics; all reductions run in a fixed order), except that
- *    vn_reduce_metric sums in another order when its temporary buffer cannot
- *    be allocated (see there).
+ *    every call (no atomics; all reductions run in a fixed order that depends
+ *    only on the sizes).
  *  - Calls that write overlapping outputs on the same device must be ordered
  *    by the caller (same stream or events).
  */
@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define VN_ABI_VERSION 1
+#define VN_ABI_VERSION 2
 
 typedef enum vn_status {
   VN_OK = 0,
@@ -212,19 +212,30 @@ int vn_flat_gradient(const float* fitness, const void* seeds, int32_t seed_dtype
                      float* grad, void* stream);
 
 /*
+ * Device workspace, in bytes, that vn_reduce_metric needs for (pop, n_params):
+ * 0 from 512 individuals on or below 131072 parameters, otherwise
+ * pop * segments * 4 with pop * segments < 1536 (at most 6 KiB).
+ *   bytes_out  HOST
+ * Errors: VN_ERR_NULL (bytes_out), VN_ERR_SHAPE (negative size).
+ */
+int vn_reduce_metric_workspace_size(int64_t pop, int64_t n_params, int64_t* bytes_out);
+
+/*
  * Mean-absolute reduction metric (API entry virtual_reduce_metric):
  *   out[i] = (1/n_params) sum_k | center[k] + sigma noise_i[offset + k] |
- *   center (n_params,) fp32;  out (pop,) fp32;  n_params > 0 when pop > 0.
- * A population below 512 splits each individual's sum into segments whose
- * partial sums go to a temporary buffer taken from the device's stream-ordered
- * allocator on `stream` and returned on it (pop * segments * 4 bytes, at most
- * 6 KiB); if that allocation fails the call proceeds with one workgroup per
- * individual, whose sums run in another order (the same means up to fp32
- * rounding).  Every sum has a fixed order: repeated calls that get the buffer
- * (or that need none: pop >= 512 or n_params < 131072) are bit-identical.
+ *   center     (n_params,) fp32;  out (pop,) fp32;  n_params > 0 when pop > 0.
+ *   workspace  DEVICE scratch of workspace_bytes >= vn_reduce_metric_workspace_size
+ *              (may be NULL when that size is 0); 4-byte aligned.  A population
+ *              below 512 splits each individual's sum into segments whose partial
+ *              sums go there; its contents on entry do not matter, and calls that
+ *              share a workspace must be ordered by the caller.
+ * Every sum has a fixed order for each (pop, n_params), so repeated calls are
+ * bit-identical.  Errors: VN_ERR_NULL for a missing workspace, VN_ERR_SHAPE for
+ * one smaller than needed.
  */
 int vn_reduce_metric(const float* center, const void* seeds, int32_t seed_dtype, int64_t pop,
-                     int64_t n_params, float sigma, int64_t offset, float* out, void* stream);
+                     int64_t n_params, float sigma, int64_t offset, float* out,
+                     void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * Noise readout (API entry _cpu_normal_noise, here on the GPU with the same

@@ -153,14 +153,34 @@ def test_metric_and_noise_validation(lib):
     E = _lib
     m = lambda **kw: lib.vn_reduce_metric(kw.get("c", FAKE), kw.get("s", FAKE), kw.get("sdt", 0),
                                           kw.get("pop", 3), kw.get("n", 5), kw.get("sigma", 0.1),
-                                          kw.get("offset", 0), kw.get("out", FAKE), None)
+                                          kw.get("offset", 0), kw.get("out", FAKE), kw.get("ws", NULL),
+                                          kw.get("ws_bytes", 0), None)
     assert m(sdt=4) == E.VN_ERR_DTYPE
     assert m(pop=-1) == E.VN_ERR_SHAPE
     assert m(n=0) == E.VN_ERR_SHAPE
+    assert m(ws_bytes=-4) == E.VN_ERR_SHAPE
     assert m(sigma=float("inf")) == E.VN_ERR_VALUE
     assert m(offset=-1) == E.VN_ERR_VALUE
     assert m(c=NULL) == E.VN_ERR_NULL
+    assert m(ws=ctypes.c_void_p(0x10002), ws_bytes=64) == E.VN_ERR_ALIGN
     assert m(pop=0, c=NULL, out=NULL) == E.VN_OK
+    # a small population over a long vector splits into segments and needs the workspace
+    need = ctypes.c_int64(-1)
+    assert lib.vn_reduce_metric_workspace_size(3, 600001, ctypes.byref(need)) == E.VN_OK
+    assert 0 < need.value <= 6 * 1024 and need.value % 4 == 0
+    assert m(n=600001) == E.VN_ERR_NULL
+    assert m(n=600001, ws=FAKE, ws_bytes=need.value - 4) == E.VN_ERR_SHAPE
+    for pop, n in [(512, 10**7), (3, 5), (1, 131071), (0, 10**6), (5, 0)]:
+        assert lib.vn_reduce_metric_workspace_size(pop, n, ctypes.byref(need)) == E.VN_OK
+        assert need.value == 0, (pop, n)
+    worst = 0
+    for pop in range(1, 512):
+        for n in (131072, 10**6, 2**31):
+            assert lib.vn_reduce_metric_workspace_size(pop, n, ctypes.byref(need)) == E.VN_OK
+            worst = max(worst, need.value)
+    assert worst <= 1535 * 4
+    assert lib.vn_reduce_metric_workspace_size(-1, 5, ctypes.byref(need)) == E.VN_ERR_SHAPE
+    assert lib.vn_reduce_metric_workspace_size(1, 5, None) == E.VN_ERR_NULL
     nz = lambda **kw: lib.vn_noise_u32(kw.get("s", FAKE), kw.get("sdt", 0), kw.get("pop", 2), kw.get("n", 4),
                                        kw.get("offset", 0), kw.get("out", FAKE), None)
     assert nz(sdt=2) == E.VN_ERR_DTYPE

@@ -313,8 +313,12 @@ def virtual_reduce_metric(center: torch.Tensor, seeds: torch.Tensor, sigma: floa
         raise ValueError("center must be 1-D with n_params elements")
     c = center.to(torch.float32).contiguous()
     o = torch.empty((s.shape[0],), dtype=torch.float32, device=dev)
+    need = ctypes.c_int64(0)
+    _lib.check("vn_reduce_metric_workspace_size",
+               lib.vn_reduce_metric_workspace_size(s.shape[0], int(n_params), ctypes.byref(need)))
+    ws = torch.empty((need.value // 4,), dtype=torch.float32, device=dev) if need.value > 0 else None
     st = lib.vn_reduce_metric(_ptr(c), _ptr(s), kind, s.shape[0], int(n_params), float(sigma), int(offset),
-                              _ptr(o), _stream(dev))
+                              _ptr(o), _ptr(ws), need.value, _stream(dev))
     _lib.check("vn_reduce_metric", st)
     return o
 

@@ -274,34 +274,38 @@ int vn_bias_gradient(const float* fitness, const void* seeds, int32_t seed_dtype
   return vn_flat_gradient(fitness, seeds, seed_dtype, pop_size, out, sigma, offset, grad_b, stream);
 }
 
+int vn_reduce_metric_workspace_size(int64_t pop, int64_t n_params, int64_t* bytes_out) {
+  if (bytes_out == nullptr) return VN_ERR_NULL;
+  if (pop < 0 || n_params < 0) return VN_ERR_SHAPE;
+  *bytes_out = pop == 0 || n_params == 0 ? 0 : vn::reduce_metric_workspace_floats(pop, n_params) * 4;
+  return VN_OK;
+}
+
 int vn_reduce_metric(const float* center, const void* seeds, int32_t seed_dtype, int64_t pop, int64_t n_params,
-                     float sigma, int64_t offset, float* out, void* stream) {
+                     float sigma, int64_t offset, float* out, void* workspace, int64_t workspace_bytes,
+                     void* stream) {
   bool i32 = false;
   int st = seed_kind(seed_dtype, &i32);
   if (st != VN_OK) return st;
-  if (pop < 0 || n_params < 0) return VN_ERR_SHAPE;
+  if (pop < 0 || n_params < 0 || workspace_bytes < 0) return VN_ERR_SHAPE;
   if (!std::isfinite(sigma) || offset < 0) return VN_ERR_VALUE;
   int64_t last;
   if (!add_ok(offset, n_params, &last)) return VN_ERR_OVERFLOW;
   if (pop == 0) return VN_OK;
   if (n_params == 0) return VN_ERR_SHAPE;  // the mean of nothing is undefined
   if (center == nullptr || seeds == nullptr || out == nullptr) return VN_ERR_NULL;
-  if (!aligned(center, 4) || !aligned(out, 4) || !aligned(seeds, i32 ? 4 : 8)) return VN_ERR_ALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!aligned(center, 4) || !aligned(out, 4) || !aligned(seeds, i32 ? 4 : 8) || !aligned(workspace, 4))
+    return VN_ERR_ALIGN;
   // A population too small to fill the GPU with one workgroup per individual
-  // splits each individual into segments; their partial sums live in a
-  // stream-ordered temporary buffer.  Without it (allocation failed) one
-  // workgroup per individual computes the same means, summed in another order
-  // (equal up to fp32 rounding).
-  const int64_t ws = vn::reduce_metric_workspace_floats(pop, n_params);
-  float* work = nullptr;
-  if (ws > 0 && hipMallocAsync(reinterpret_cast<void**>(&work), static_cast<size_t>(ws) * sizeof(float), s) != hipSuccess) {
-    work = nullptr;
-    (void)hipGetLastError();
-  }
-  const hipError_t e = vn::launch_reduce_metric(center, seeds, i32, pop, n_params, sigma, offset, out, work, s);
-  if (work != nullptr) (void)hipFreeAsync(work, s);
-  return hip_status(e);
+  // splits each individual into segments whose partial sums go to the
+  // caller's workspace (vn_reduce_metric_workspace_size); there is one
+  // summation order for each (pop, n_params).
+  const int64_t need = vn::reduce_metric_workspace_floats(pop, n_params) * 4;
+  if (need > 0 && workspace == nullptr) return VN_ERR_NULL;
+  if (workspace_bytes < need) return VN_ERR_SHAPE;
+  return hip_status(vn::launch_reduce_metric(center, seeds, i32, pop, n_params, sigma, offset, out,
+                                             need > 0 ? static_cast<float*>(workspace) : nullptr,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 static int noise_common(const void* seeds, int32_t seed_dtype, int64_t pop, int64_t n, int64_t offset,

@@ -68,8 +68,8 @@ hipError_t launch_noise(const void* seeds, bool seeds_i32, int64_t pop, int64_t 
                         uint32_t* r_out, float* n_out, hipStream_t stream);
 // Floats of workspace the reduce metric uses for (pop, n); 0 = none needed.
 int64_t reduce_metric_workspace_floats(int64_t pop, int64_t n);
-// workspace: reduce_metric_workspace_floats(pop, n) floats, or null (one
-// workgroup per individual then).
+// workspace: reduce_metric_workspace_floats(pop, n) floats (null when that
+// is 0).
 hipError_t launch_reduce_metric(const float* center, const void* seeds, bool seeds_i32, int64_t pop,
                                 int64_t n, float sigma, int64_t offset, float* out, float* workspace,
                                 hipStream_t stream);

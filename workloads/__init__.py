@@ -92,28 +92,29 @@ def centered_ranks(raw: np.ndarray) -> np.ndarray:
     return (ranks / (p - 1) - 0.5).astype(np.float32)
 
 
-def _chain(shapes_io, biases):
-    """Lay out [W1, b1, W2, b2, ...] back to back; returns per-layer offsets and
-    the block shape list (the bias block follows its weight block)."""
+# Flat noise offsets of every parameter block, written out (weights then bias
+# of each layer, back to back, as the page's compute_offsets example lays out
+# an MLP's blocks): per layer (weight offset, bias offset).  Written as
+# literals so that this module computes no part of the method; the tests check
+# them against compute_offsets of the block shapes.
+LAYER_OFFSETS = {
+    1: [(0, 2048)],                                          # 64 -> 32 with bias
+    2: [(0, 1048576)],                                       # 1024 -> 1024 with bias
+    3: [(0, 131072)],                                        # 512 -> 256, no bias
+    4: [(0, 200704), (200960, 266496), (266752, 269312)],   # 784 -> 256 -> 256 -> 10, biases
+    5: [(0, 16777216)],                                      # 4096 -> 4096, no bias
+    6: [(0, 16777216)],                                      # 4096 -> 4096, no bias
+}
+
+
+def _block_shapes(shapes_io, biases):
+    """[(out, in), (out,)?, ...] in flat order."""
     shapes = []
     for (i, o), has_b in zip(shapes_io, biases):
         shapes.append((o, i))
         if has_b:
             shapes.append((o,))
-    # plain running sum of block sizes
-    offs, run = [], 0
-    for s in shapes:
-        offs.append(run)
-        run += int(np.prod(s))
-    per_layer, t = [], 0
-    for (i, o), has_b in zip(shapes_io, biases):
-        w_off = offs[t]
-        t += 1
-        b_off = w_off + o * i
-        if has_b:
-            t += 1
-        per_layer.append((w_off, b_off))
-    return per_layer, shapes
+    return shapes
 
 
 DESCRIPTIONS = {
@@ -135,7 +136,7 @@ def make(key: int) -> Workload:
         w = _normal(rng, (fout, fin), 1.0 / fin)
         b = _normal(rng, (fout,), 0.01)
         fit = _normal(rng, (pop,))
-        per, shapes = _chain([(fin, fout)], [True])
+        per, shapes = LAYER_OFFSETS[1], _block_shapes([(fin, fout)], [True])
         return Workload(1, DESCRIPTIONS[1], pop, batch, "f32", np.arange(pop, dtype=np.int64),
                         0.02, x, [Layer(w, b, *per[0])], fit, shapes=shapes)
     if key == 2:
@@ -144,7 +145,7 @@ def make(key: int) -> Workload:
         w = _normal(rng, (fout, fin), 1.0 / fin)
         b = np.zeros(fout, dtype=np.float32)
         fit = centered_ranks(_normal(rng, (pop,)))
-        per, shapes = _chain([(fin, fout)], [True])
+        per, shapes = LAYER_OFFSETS[2], _block_shapes([(fin, fout)], [True])
         return Workload(2, DESCRIPTIONS[2], pop, batch, "f32",
                         1000 + np.arange(pop, dtype=np.int64), 0.01, x,
                         [Layer(w, b, *per[0])], fit, shapes=shapes)
@@ -153,7 +154,7 @@ def make(key: int) -> Workload:
         x = _uniform(rng, (pop, batch, fin), -1.0, 1.0)
         w = _normal(rng, (fout, fin), 1.0 / fin)
         fit = _normal(rng, (pop,))
-        per, shapes = _chain([(fin, fout)], [False])
+        per, shapes = LAYER_OFFSETS[3], _block_shapes([(fin, fout)], [False])
         return Workload(3, DESCRIPTIONS[3], pop, batch, "f32", np.arange(pop, dtype=np.int64),
                         0.05, x, [Layer(w, None, *per[0])], fit, shapes=shapes)
     if key == 4:
@@ -163,7 +164,7 @@ def make(key: int) -> Workload:
         ws = [_normal(rng, (o, i), 1.0 / i) for i, o in dims]
         bs = [np.zeros(o, dtype=np.float32) for _, o in dims]
         fit = _normal(rng, (pop,))
-        per, shapes = _chain(dims, [True, True, True])
+        per, shapes = LAYER_OFFSETS[4], _block_shapes(dims, [True, True, True])
         layers = [Layer(w, b, *p) for w, b, p in zip(ws, bs, per)]
         return Workload(4, DESCRIPTIONS[4], pop, batch, "f32", np.arange(pop, dtype=np.int64),
                         0.02, x, layers, fit, relu_between=True, shapes=shapes)
@@ -172,7 +173,7 @@ def make(key: int) -> Workload:
         x = round_to_bf16(_normal(rng, (pop, batch, fin)))
         w = round_to_bf16(_normal(rng, (fout, fin), 1.0 / fin))
         fit = _normal(rng, (pop,))
-        per, shapes = _chain([(fin, fout)], [False])
+        per, shapes = LAYER_OFFSETS[5], _block_shapes([(fin, fout)], [False])
         return Workload(5, DESCRIPTIONS[5], pop, batch, "bf16", np.arange(pop, dtype=np.int64),
                         0.001, x, [Layer(w, None, *per[0])], fit, shapes=shapes)
     if key == 6:
@@ -182,7 +183,7 @@ def make(key: int) -> Workload:
         x = round_to_bf16(_normal(rng, (batch, fin)))
         w = round_to_bf16(_normal(rng, (fout, fin), 1.0 / fin))
         fit = _normal(rng, (pop,))
-        per, shapes = _chain([(fin, fout)], [False])
+        per, shapes = LAYER_OFFSETS[6], _block_shapes([(fin, fout)], [False])
         return Workload(6, DESCRIPTIONS[6], pop, batch, "bf16", np.arange(pop, dtype=np.int64),
                         0.001, x, [Layer(w, None, *per[0])], fit, shapes=shapes)
     raise ValueError(f"unknown workload {key}")
