@@ -238,6 +238,21 @@ int vn_reduce_metric(const float* center, const void* seeds, int32_t seed_dtype,
                      void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * vn_reduce_metric without a caller workspace and without any allocation, for
+ * callers that cannot allocate device memory (code under stream capture into
+ * a graph, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, result and summation order as vn_reduce_metric.  Its partial sums
+ * live in a fixed array of 8 KiB in each GPU's memory, held from the first
+ * call on that GPU until the process ends; every (pop, n_params) needs at most
+ * 6 KiB of it (VN_ERR_OVERFLOW would report a larger need).  All calls on one
+ * GPU share that array: calls that may overlap on one GPU (different streams,
+ * other threads) race and must be ordered by the caller.  VN_ERR_HIP if the
+ * array's address cannot be obtained.
+ */
+int vn_reduce_metric_noalloc(const float* center, const void* seeds, int32_t seed_dtype, int64_t pop,
+                             int64_t n_params, float sigma, int64_t offset, float* out, void* stream);
+
+/*
  * Noise readout (API entry _cpu_normal_noise, here on the GPU with the same
  * device hash as every kernel above; for verification):
  *   r_out[i,t] = low 32 bits of the hash of (seed_i, offset + t)       (pop, n) uint32

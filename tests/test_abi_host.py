@@ -181,6 +181,19 @@ def test_metric_and_noise_validation(lib):
     assert worst <= 1535 * 4
     assert lib.vn_reduce_metric_workspace_size(-1, 5, ctypes.byref(need)) == E.VN_ERR_SHAPE
     assert lib.vn_reduce_metric_workspace_size(1, 5, None) == E.VN_ERR_NULL
+    # the allocation-free variant validates the same way before any HIP call
+    na = lambda **kw: lib.vn_reduce_metric_noalloc(kw.get("c", FAKE), kw.get("s", FAKE), kw.get("sdt", 0),
+                                                   kw.get("pop", 3), kw.get("n", 5), kw.get("sigma", 0.1),
+                                                   kw.get("offset", 0), kw.get("out", FAKE), None)
+    assert na(sdt=4) == E.VN_ERR_DTYPE
+    assert na(pop=-1) == E.VN_ERR_SHAPE
+    assert na(n=0) == E.VN_ERR_SHAPE
+    assert na(sigma=float("nan")) == E.VN_ERR_VALUE
+    assert na(offset=-1) == E.VN_ERR_VALUE
+    assert na(offset=2**63 - 2) == E.VN_ERR_OVERFLOW
+    assert na(out=NULL) == E.VN_ERR_NULL
+    assert na(c=ctypes.c_void_p(0x10002)) == E.VN_ERR_ALIGN
+    assert na(pop=0, c=NULL, out=NULL) == E.VN_OK
     nz = lambda **kw: lib.vn_noise_u32(kw.get("s", FAKE), kw.get("sdt", 0), kw.get("pop", 2), kw.get("n", 4),
                                        kw.get("offset", 0), kw.get("out", FAKE), None)
     assert nz(sdt=2) == E.VN_ERR_DTYPE

@@ -28,6 +28,7 @@ __all__ = [
     "virtual_bias_gradient",
     "virtual_flat_gradient",
     "virtual_reduce_metric",
+    "virtual_reduce_metric_noalloc",
     "noise_u32",
     "noise_f32",
     "VNError",
@@ -320,6 +321,32 @@ def virtual_reduce_metric(center: torch.Tensor, seeds: torch.Tensor, sigma: floa
     st = lib.vn_reduce_metric(_ptr(c), _ptr(s), kind, s.shape[0], int(n_params), float(sigma), int(offset),
                               _ptr(o), _ptr(ws), need.value, _stream(dev))
     _lib.check("vn_reduce_metric", st)
+    return o
+
+
+def virtual_reduce_metric_noalloc(center: torch.Tensor, seeds: torch.Tensor, sigma: float, n_params: int,
+                                  offset: int = 0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``virtual_reduce_metric`` through the entry point that allocates nothing:
+    its partial sums live in a fixed array on the GPU (``vn_reduce_metric_noalloc``).
+    With ``out`` given, the call makes no allocation at all; calls on one GPU that
+    may overlap must be ordered by the caller."""
+    lib = _lib.load()
+    _require_device("center", center)
+    dev = center.device
+    s, kind = _seeds(seeds, dev)
+    if center.dim() != 1 or center.shape[0] != int(n_params):
+        raise ValueError("center must be 1-D with n_params elements")
+    c = center.to(torch.float32).contiguous()
+    if out is None:
+        o = torch.empty((s.shape[0],), dtype=torch.float32, device=dev)
+    else:
+        _require_device("out", out, dev)
+        if out.shape != (s.shape[0],) or out.dtype != torch.float32 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float32 (pop,) tensor")
+        o = out
+    st = lib.vn_reduce_metric_noalloc(_ptr(c), _ptr(s), kind, s.shape[0], int(n_params), float(sigma),
+                                      int(offset), _ptr(o), _stream(dev))
+    _lib.check("vn_reduce_metric_noalloc", st)
     return o
 
 

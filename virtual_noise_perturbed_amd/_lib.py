@@ -38,6 +38,8 @@ SIGNATURES = {
     "vn_reduce_metric_workspace_size": [c_int64, c_int64, c_void_p],
     "vn_reduce_metric": [c_void_p, c_void_p, c_int32, c_int64, c_int64, c_float, c_int64,
                          c_void_p, c_void_p, c_int64, c_void_p],
+    "vn_reduce_metric_noalloc": [c_void_p, c_void_p, c_int32, c_int64, c_int64, c_float, c_int64,
+                                 c_void_p, c_void_p],
     "vn_noise_u32": [c_void_p, c_int32, c_int64, c_int64, c_int64, c_void_p, c_void_p],
     "vn_noise_f32": [c_void_p, c_int32, c_int64, c_int64, c_int64, c_void_p, c_void_p],
 }

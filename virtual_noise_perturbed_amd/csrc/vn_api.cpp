@@ -308,6 +308,30 @@ int vn_reduce_metric(const float* center, const void* seeds, int32_t seed_dtype,
                                              static_cast<hipStream_t>(stream)));
 }
 
+int vn_reduce_metric_noalloc(const float* center, const void* seeds, int32_t seed_dtype, int64_t pop,
+                             int64_t n_params, float sigma, int64_t offset, float* out, void* stream) {
+  bool i32 = false;
+  int st = seed_kind(seed_dtype, &i32);
+  if (st != VN_OK) return st;
+  if (pop < 0 || n_params < 0) return VN_ERR_SHAPE;
+  if (!std::isfinite(sigma) || offset < 0) return VN_ERR_VALUE;
+  int64_t last;
+  if (!add_ok(offset, n_params, &last)) return VN_ERR_OVERFLOW;
+  if (pop == 0) return VN_OK;
+  if (n_params == 0) return VN_ERR_SHAPE;
+  if (center == nullptr || seeds == nullptr || out == nullptr) return VN_ERR_NULL;
+  if (!aligned(center, 4) || !aligned(out, 4) || !aligned(seeds, i32 ? 4 : 8)) return VN_ERR_ALIGN;
+  const int64_t need = vn::reduce_metric_workspace_floats(pop, n_params);
+  if (need > vn::kMetricScratchFloats) return VN_ERR_OVERFLOW;   // beyond the fixed scratch array
+  float* work = nullptr;
+  if (need > 0) {
+    const hipError_t e = vn::metric_scratch_address(&work);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return hip_status(vn::launch_reduce_metric(center, seeds, i32, pop, n_params, sigma, offset, out, work,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 static int noise_common(const void* seeds, int32_t seed_dtype, int64_t pop, int64_t n, int64_t offset,
                         uint32_t* r_out, float* n_out, void* out_ptr, void* stream) {
   bool i32 = false;

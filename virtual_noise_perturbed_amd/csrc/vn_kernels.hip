@@ -46,6 +46,7 @@
 //    tiles of one individual, which share its X rows, run one after another
 //    on one XCD (xcd_remap, individual_major_order).
 
+#include <mutex>
 #include <type_traits>
 
 #include "vn_device.hpp"
@@ -1816,6 +1817,33 @@ static int64_t metric_segments(int64_t pop, int64_t n) {
 int64_t reduce_metric_workspace_floats(int64_t pop, int64_t n) {
   const int64_t seg = metric_segments(pop, n);
   return seg > 1 ? pop * seg : 0;
+}
+
+// Partial sums of the allocation-free reduce metric: one array per GPU,
+// alive until the process ends.  Every call on a GPU uses that GPU's copy
+// (calls that overlap on one GPU race); each call writes every slot it
+// reads before reading it, so nothing needs clearing between calls.
+static __device__ __align__(256) float scratch[kMetricScratchFloats];
+
+hipError_t metric_scratch_address(float** ptr) {
+  // The address of a device's copy, looked up once per device with that
+  // device current (host code must not use the array's name itself).
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float*>(a);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_reduce_metric(const float* center, const void* seeds, bool seeds_i32, int64_t pop, int64_t n,

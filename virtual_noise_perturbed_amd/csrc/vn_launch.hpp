@@ -74,6 +74,12 @@ hipError_t launch_reduce_metric(const float* center, const void* seeds, bool see
                                 int64_t n, float sigma, int64_t offset, float* out, float* workspace,
                                 hipStream_t stream);
 
+// Floats in each GPU's allocation-free reduce-metric scratch array: more than
+// the most any (pop, n) needs (pop * segments < 1536, see metric_segments).
+constexpr int64_t kMetricScratchFloats = 2048;
+// Device address of the current GPU's scratch array (looked up once per device).
+hipError_t metric_scratch_address(float** ptr);
+
 // Largest grid.x the launchers use (they loop inside the kernel beyond it).
 constexpr int64_t kMaxGridX = 0x7FFFFFFF;
 
