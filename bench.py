@@ -38,17 +38,22 @@ METRIC = "perturbed-linear TFLOP/s + noise-gradient elements/s, % of roofline, 1
 # v_mov_b32], then v_alignbit_b32 + v_bitop3_b32 for the low word with the
 # sign flip), v_ashrrev_i32 for N * 2^24 and v_cvt_f32_i32 -- and consume it
 # with at least one fma.  virtual_noise_perturbed_amd/vn_probe measures that
-# exact sequence ("noise_fma": eight independent Weyl-stepped chains per lane,
-# 8 waves per SIMD, nothing else) and reads the shader clock of the launch
-# (which moves between 2.0 and 2.43 GHz under load): 16.96 to 17.53
-# lane-cycles per element per CU over runs, the lowest taken (summary in
-# profiles/vn_probe_gfx950.txt).  The peak prices
-# that per-cycle cost at the nominal 2.4 GHz on 256 CUs x 64 lanes.  (Summing
-# the instructions' isolated issue costs gives 17.9: mixed, they overlap a
-# little.)
+# exact sequence (nothing else in the loop, independent Weyl-stepped chains
+# per lane, 2 to 8 waves per SIMD) and reads the shader clock of each launch
+# (which moves between 2.0 and 2.43 GHz under load).  The peak prices the
+# lowest per-cycle cost in the committed probe runs (profiles/vn_probe_gfx950.txt:
+# 16.69 lane-cycles per element, one chain per lane at 8 waves per SIMD; the
+# same runs give 16.69-17.28 over occupancies of 8 waves) at the nominal
+# 2.4 GHz on 256 CUs x 64 lanes.
 CLOCK_HZ = 2.4e9
-NOISE_LANE_CYCLES = 16.96   # per element per CU lane, at the measured clock (vn_probe noise_fma)
+NOISE_LANE_CYCLES = 16.69   # per element per CU lane, at the measured clock (vn_probe, lowest committed)
 HASH_PEAK_PER_S = 256 * 64 * CLOCK_HZ / NOISE_LANE_CYCLES
+# The same sequence priced by the sum of its 20 instructions' isolated issue
+# costs (the per-instruction rates of the same probe runs): a floor set by
+# instruction counts alone.  Mixed, the instructions overlap a little, so this
+# peak is lower than the measured one above.
+ISSUE_SUM_LANE_CYCLES = 18.57
+ISSUE_SUM_PEAK_PER_S = 256 * 64 * CLOCK_HZ / ISSUE_SUM_LANE_CYCLES
 HBM_PEAK_GBS = 8000.0
 HBM_PEAK = HBM_PEAK_GBS * 1e9   # bytes/s
 MFMA_BF16_PEAK = 2.5e15    # dense bf16 matrix-core FLOP/s
@@ -537,6 +542,9 @@ def main():
             "peak_basis": (f"noise generation bound: {NOISE_LANE_CYCLES} lane-cycles per noise element "
                            f"(state step, hash, N as fp32, one fma; measured per shader-clock cycle), "
                            f"256 CUs x 64 lanes x 2.4 GHz"),
+            "frac_vs_issue_sum": round(achieved / ISSUE_SUM_PEAK_PER_S, 4),
+            "issue_sum_basis": (f"{ISSUE_SUM_LANE_CYCLES} lane-cycles per element: the isolated issue costs of "
+                                f"the sequence's 20 instructions summed"),
             "fractions": fractions,
         }
 

@@ -70,3 +70,17 @@ def test_committed_traffic_record_matches_the_kernels(bench):
         assert bench.recorded_traffic(5, "forward0") is None
         pytest.skip("kernel sources changed since the traffic counters were taken: bench.py reports null")
     assert bench.recorded_traffic(5, "forward0") is not None
+
+
+def test_build_scratch_check_reads_the_resource_remarks():
+    """The build's scratch check picks out kernels with nonzero ScratchSize
+    from the compiler's resource-usage remarks (format of hipcc's output)."""
+    from virtual_noise_perturbed_amd import build as b
+    remarks = "\n".join([
+        "vn_kernels.hip:10:1: remark: Function Name: _ZN2vn1aEv [-Rpass-analysis=kernel-resource-usage]",
+        "vn_kernels.hip:10:1: remark:     VGPRs: 128 [-Rpass-analysis=kernel-resource-usage]",
+        "vn_kernels.hip:10:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "vn_kernels.hip:20:1: remark: Function Name: _ZN2vn1bEv [-Rpass-analysis=kernel-resource-usage]",
+        "vn_kernels.hip:20:1: remark:     ScratchSize [bytes/lane]: 128 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert b.kernels_with_scratch(remarks) == {"_ZN2vn1bEv": 128}

@@ -40,20 +40,49 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libvn.so)")
 
 
+# the compiler's per-kernel resource report (registers, scratch, occupancy)
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+
+
+def kernels_with_scratch(remarks: str) -> dict:
+    """Kernel name -> scratch bytes per lane, for every kernel whose resource
+    report (the compiler's kernel-resource-usage remarks) shows scratch."""
+    import re
+    found, name = {}, None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name is not None and int(m.group(1)) > 0:
+            found[name] = int(m.group(1))
+    return found
+
+
 def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every source and link libvn.so; returns its path."""
+    """Compile every source and link libvn.so; returns its path.  Fails when
+    any kernel spills to scratch memory (per-lane stack traffic in the hot
+    loops is never intended here)."""
     out_tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-shared", "-I", INCLUDE, "-I", CSRC,
+    cmd = [hipcc(), *HIPCC_FLAGS, RESOURCE_REMARKS, *(extra_flags or []), "-shared", "-I", INCLUDE, "-I", CSRC,
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out_tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass of hipcc does not know the packed-fp32 feature and says so; harmless
-    errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+    lines = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l]
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
-    if verbose and errs.strip():
-        print(errs, file=sys.stderr)
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n" + "\n".join(lines))
+    # (the resource remarks come with source excerpts; only real diagnostics are shown)
+    diags = "\n".join(l for l in lines if ("warning:" in l or "error:" in l) and "kernel-resource-usage" not in l)
+    if verbose and diags.strip():
+        print(diags, file=sys.stderr)
+    spills = kernels_with_scratch(res.stderr)
+    if spills:
+        os.remove(out_tmp)
+        raise RuntimeError("kernels use scratch memory (register spills): " +
+                           ", ".join(f"{k} ({v} B/lane)" for k, v in sorted(spills.items())))
     os.replace(out_tmp, LIB)
     build_probe(verbose)
     return LIB

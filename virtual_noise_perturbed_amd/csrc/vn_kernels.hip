@@ -1170,7 +1170,7 @@ __global__ __launch_bounds__(512, 4) void forward_chain_kernel(ChainParams p) {
   using Acc = typename MF::Acc;
   constexpr int WAVES = 8, NTHR = 64 * WAVES;
   constexpr int MB = 2;                        // 64 rows
-  constexpr int R = 16;                        // k per lane per chunk
+  constexpr int R = SPLIT ? 8 : 16;            // k per lane per chunk (fp32 operands: hi and lo runs, half as long)
   constexpr int T = R / 8;
   constexpr int KC = MF::H * R;                // 32
   constexpr int ROWS = MB * 32;
