@@ -59,6 +59,7 @@ HBM_PEAK = HBM_PEAK_GBS * 1e9   # bytes/s
 MFMA_BF16_PEAK = 2.5e15    # dense bf16 matrix-core FLOP/s
 
 KERNEL_SRC = os.path.join(ROOT, "virtual_noise_perturbed_amd", "csrc", "vn_kernels.hip")
+GEMM_SRC = os.path.join(ROOT, "virtual_noise_perturbed_amd", "csrc", "vn_gemm.hip")
 DEVICE_SRC = os.path.join(ROOT, "virtual_noise_perturbed_amd", "csrc", "vn_device.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -76,7 +77,7 @@ def code_without_comments(text: str) -> str:
 def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in (KERNEL_SRC, DEVICE_SRC):
+    for f in (KERNEL_SRC, GEMM_SRC, DEVICE_SRC):
         with open(f, encoding="utf-8") as fh:
             h.update(code_without_comments(fh.read()).encode())
     return h.hexdigest()[:16]

@@ -26,8 +26,8 @@
  * Conventions for every entry point below:
  *  - All pointers except those of vn_compute_offsets are DEVICE pointers owned
  *    by the caller.  The library keeps no state and allocates no memory: the
- *    one entry point that needs scratch space (vn_reduce_metric) takes it from
- *    the caller.
+ *    entry points that use scratch space (vn_reduce_metric, and
+ *    vn_perturbed_linear for large batches) take it from the caller.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = null stream).
  *    VN_OK means "validated and enqueued"; outputs are valid once the stream
  *    reaches the launch.  Arguments are validated before any HIP call and a
@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define VN_ABI_VERSION 2
+#define VN_ABI_VERSION 3
 
 typedef enum vn_status {
   VN_OK = 0,
@@ -130,15 +130,37 @@ int vn_compute_offsets(const int64_t* dims, const int32_t* ndims, int32_t n_bloc
  *   activation    VN_ACT_NONE or VN_ACT_RELU
  *   math          vn_math (VN_MATH_F32 requires dtype VN_F32)
  *   y             (pop, batch, out) fp32 output
+ *   workspace     DEVICE scratch of workspace_bytes (16-byte aligned), or NULL
+ *                 with workspace_bytes 0.  When it holds at least
+ *                 vn_perturbed_linear_workspace_size bytes for these sizes (bf16
+ *                 operands and many rows per individual; 16-byte aligned x and
+ *                 w), the perturbed weights of groups of individuals are formed
+ *                 there once and multiplied on the matrix cores; otherwise the
+ *                 noise is generated inside the product.  Both give the same
+ *                 bits.  The library only reads what it wrote there during the
+ *                 call; calls sharing a workspace must be ordered by the caller.
  * W + sigma*N is always formed in fp32 (one fma).  The bf16 variant rounds it
  * to bf16 (nearest even) before the product; the fp32 variant keeps it to
  * about 16 significant bits (VN_MATH_DEFAULT) or to fp32 (VN_MATH_F32).
+ * Errors also: VN_ERR_SHAPE for workspace_bytes < 0, VN_ERR_ALIGN for a
+ * workspace not 16-byte aligned.
  */
 int vn_perturbed_linear(const void* x, int64_t x_pop_stride, const void* w, int32_t dtype,
                         const float* bias, const void* seeds, int32_t seed_dtype,
                         int64_t pop, int64_t batch, int64_t in, int64_t out,
                         float sigma, int64_t offset, int32_t activation, int32_t math,
-                        float* y, void* stream);
+                        float* y, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Device workspace, in bytes, with which vn_perturbed_linear takes its
+ * materialized-weights path for these sizes; 0 when the sizes do not take it
+ * (fp32 operands, fewer than 2048 rows per individual, in not a multiple of 64
+ * in [128, 2^22)).  At most 256 MiB, or one individual's out*in bf16 values
+ * when that is larger.  Errors: VN_ERR_NULL (bytes_out), VN_ERR_DTYPE,
+ * VN_ERR_SHAPE (negative size), VN_ERR_VALUE (math), VN_ERR_OVERFLOW.
+ */
+int vn_perturbed_linear_workspace_size(int32_t dtype, int64_t pop, int64_t batch, int64_t in, int64_t out,
+                                       int32_t math, int64_t* bytes_out);
 
 /*
  * A chain of perturbed layers in one call: the model equation applied

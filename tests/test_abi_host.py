@@ -80,11 +80,11 @@ def test_compute_offsets_errors(lib):
 
 def fwd(lib, **kw):
     a = dict(x=FAKE, stride=0, w=FAKE, dtype=_lib.VN_F32, b=NULL, seeds=FAKE, sdt=_lib.VN_I64, pop=4,
-             batch=2, i=8, o=3, sigma=0.1, offset=0, act=0, math=0, y=FAKE, stream=NULL)
+             batch=2, i=8, o=3, sigma=0.1, offset=0, act=0, math=0, y=FAKE, ws=NULL, ws_bytes=0, stream=NULL)
     a.update(kw)
     return lib.vn_perturbed_linear(a["x"], a["stride"], a["w"], a["dtype"], a["b"], a["seeds"], a["sdt"],
                                    a["pop"], a["batch"], a["i"], a["o"], a["sigma"], a["offset"], a["act"],
-                                   a["math"], a["y"], a["stream"])
+                                   a["math"], a["y"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 def test_forward_validation(lib):
@@ -111,6 +111,8 @@ def test_forward_validation(lib):
     assert fwd(lib, y=ctypes.c_void_p(0x10002)) == E.VN_ERR_ALIGN
     assert fwd(lib, seeds=ctypes.c_void_p(0x10004)) == E.VN_ERR_ALIGN
     assert fwd(lib, x=ctypes.c_void_p(0x10002)) == E.VN_ERR_ALIGN
+    assert fwd(lib, ws=FAKE, ws_bytes=-1) == E.VN_ERR_SHAPE
+    assert fwd(lib, ws=ctypes.c_void_p(0x10008), ws_bytes=64) == E.VN_ERR_ALIGN   # workspace not 16-byte aligned
     # zero extents: nothing to do, nothing launched, even with NULL outputs
     assert fwd(lib, pop=0, y=NULL, x=NULL, w=NULL, seeds=NULL) == E.VN_OK
     assert fwd(lib, batch=0, y=NULL) == E.VN_OK
@@ -262,3 +264,34 @@ def test_binding_refuses_cpu_tensors():
         vn.virtual_perturbed_linear(x, w, None, s, 0.1, 0)
     with pytest.raises(ValueError, match="GPU"):
         vn.virtual_weight_gradient(torch.zeros(2), s, (4, 3), 0.1, 2, 0)
+
+
+def ws_size(lib, dtype, pop, batch, i, o, math=0):
+    out = ctypes.c_int64(-7)
+    st = lib.vn_perturbed_linear_workspace_size(dtype, pop, batch, i, o, math, ctypes.byref(out))
+    return st, out.value
+
+
+def test_forward_workspace_size(lib):
+    E = _lib
+    mib = 1 << 20
+    # bf16 operands, many rows: groups of up to 256 MiB of perturbed weights
+    assert ws_size(lib, E.VN_BF16, 16, 4096, 4096, 4096) == (E.VN_OK, 8 * 32 * mib)
+    assert ws_size(lib, E.VN_BF16, 3, 2048, 4096, 4096) == (E.VN_OK, 3 * 32 * mib)
+    assert ws_size(lib, E.VN_BF16, 2, 2048, 16384, 16384) == (E.VN_OK, 512 * mib)   # one individual per group
+    assert ws_size(lib, E.VN_BF16, 1, 2048, 128, 1) == (E.VN_OK, 256)
+    # sizes that keep the noise inside the product: no workspace
+    assert ws_size(lib, E.VN_F32, 16, 4096, 4096, 4096) == (E.VN_OK, 0)
+    assert ws_size(lib, E.VN_BF16, 16, 2047, 4096, 4096) == (E.VN_OK, 0)
+    assert ws_size(lib, E.VN_BF16, 16, 4096, 4000, 4096) == (E.VN_OK, 0)      # in not a multiple of 64
+    assert ws_size(lib, E.VN_BF16, 16, 4096, 64, 4096) == (E.VN_OK, 0)        # in below 128
+    assert ws_size(lib, E.VN_BF16, 16, 4096, 1 << 22, 8) == (E.VN_OK, 0)     # in too wide
+    assert ws_size(lib, E.VN_BF16, 0, 4096, 4096, 4096) == (E.VN_OK, 0)
+    assert ws_size(lib, E.VN_BF16, 16, 4096, 4096, 0) == (E.VN_OK, 0)
+    # errors
+    assert lib.vn_perturbed_linear_workspace_size(E.VN_BF16, 1, 1, 1, 1, 0, None) == E.VN_ERR_NULL
+    assert ws_size(lib, 7, 1, 1, 1, 1)[0] == E.VN_ERR_DTYPE
+    assert ws_size(lib, E.VN_BF16, -1, 1, 1, 1)[0] == E.VN_ERR_SHAPE
+    assert ws_size(lib, E.VN_BF16, 1, 1, -1, 1)[0] == E.VN_ERR_SHAPE
+    assert ws_size(lib, E.VN_BF16, 1, 1, 1, 1, math=5)[0] == E.VN_ERR_VALUE
+    assert ws_size(lib, E.VN_BF16, 1, 1, 2**62, 2**62)[0] == E.VN_ERR_OVERFLOW

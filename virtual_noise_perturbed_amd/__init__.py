@@ -94,7 +94,7 @@ def virtual_perturbed_linear(x: torch.Tensor, weight: torch.Tensor, bias: Option
                              seeds: torch.Tensor, sigma: float, offset: int,
                              activation: Optional[str] = None,
                              out: Optional[torch.Tensor] = None,
-                             math: str = "default") -> torch.Tensor:
+                             math: str = "default", materialize: bool = True) -> torch.Tensor:
     """``Y[i] = X[i] @ (W + sigma*N_i)^T + (b + sigma*nb_i)`` (page entry
     ``virtual_perturbed_linear``).
 
@@ -104,6 +104,9 @@ def virtual_perturbed_linear(x: torch.Tensor, weight: torch.Tensor, bias: Option
     be ``"relu"`` to apply max(., 0) in the same kernel.  ``math``: ``"default"``
     (float32 operands as three bf16 matrix-core products, about 2^-16 relative
     per product) or ``"f32"`` (float32 matrix-core products; float32 only).
+    ``materialize``: give the library the device workspace it asks for, so
+    that large bf16 batches take the materialized-weights path (same bits;
+    False keeps the noise inside the product).
     """
     lib = _lib.load()
     _require_device("weight", weight)
@@ -155,9 +158,14 @@ def virtual_perturbed_linear(x: torch.Tensor, weight: torch.Tensor, bias: Option
         if out.shape != (pop, batch, out_f) or out.dtype != torch.float32 or not out.is_contiguous():
             raise ValueError("out must be a contiguous float32 (pop, batch, out) tensor")
         y = out
+    need = ctypes.c_int64(0)
+    if materialize:
+        _lib.check("vn_perturbed_linear_workspace_size",
+                   lib.vn_perturbed_linear_workspace_size(dt, pop, batch, in_f, out_f, mm, ctypes.byref(need)))
+    ws = torch.empty((need.value,), dtype=torch.uint8, device=dev) if need.value > 0 else None
     st = lib.vn_perturbed_linear(_ptr(xc), stride, _ptr(wc), dt, _ptr(b), _ptr(s), kind,
                                  pop, batch, in_f, out_f, float(sigma), int(offset), act, mm,
-                                 _ptr(y), _stream(dev))
+                                 _ptr(y), _ptr(ws), need.value, _stream(dev))
     _lib.check("vn_perturbed_linear", st)
     return y
 

@@ -26,7 +26,8 @@ SIGNATURES = {
     "vn_compute_offsets": [c_void_p, c_void_p, c_int32, c_void_p, c_void_p],
     "vn_perturbed_linear": [c_void_p, c_int64, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
                             c_int64, c_int64, c_int64, c_int64, c_float, c_int64, c_int32, c_int32,
-                            c_void_p, c_void_p],
+                            c_void_p, c_void_p, c_int64, c_void_p],
+    "vn_perturbed_linear_workspace_size": [c_int32, c_int64, c_int64, c_int64, c_int64, c_int32, c_void_p],
     "vn_perturbed_mlp": [c_void_p, c_int64, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                          c_void_p, c_int32, c_int64, c_int64, c_float, c_int32, c_void_p, c_void_p],
     "vn_weight_gradient": [c_void_p, c_void_p, c_int32, c_int64, c_int64, c_int64, c_float, c_int64,

@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libvn.so")
 PROBE = os.path.join(PKG, "vn_probe")
 ARCH = "gfx950"
 
-SOURCES = ["vn_kernels.hip", "vn_api.cpp"]
+SOURCES = ["vn_kernels.hip", "vn_gemm.hip", "vn_api.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

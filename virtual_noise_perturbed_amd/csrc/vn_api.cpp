@@ -118,10 +118,24 @@ int vn_compute_offsets(const int64_t* dims, const int32_t* ndims, int32_t n_bloc
   return VN_OK;
 }
 
+int vn_perturbed_linear_workspace_size(int32_t dtype, int64_t pop, int64_t batch, int64_t in, int64_t out,
+                                       int32_t math, int64_t* bytes_out) {
+  if (bytes_out == nullptr) return VN_ERR_NULL;
+  if (dtype != VN_F32 && dtype != VN_BF16) return VN_ERR_DTYPE;
+  if (pop < 0 || batch < 0 || in < 0 || out < 0) return VN_ERR_SHAPE;
+  if (math != VN_MATH_DEFAULT && math != VN_MATH_F32) return VN_ERR_VALUE;
+  int64_t oi;
+  if (!mul_ok(out, in, &oi) || !mul_ok(oi, 2, &oi)) return VN_ERR_OVERFLOW;
+  *bytes_out = 0;
+  if (dtype == VN_BF16 && math == VN_MATH_DEFAULT && pop > 0 && vn::materialized_forward_applies(batch, in, out))
+    *bytes_out = vn::materialized_workspace_bytes(pop, batch, in, out);
+  return VN_OK;
+}
+
 int vn_perturbed_linear(const void* x, int64_t x_pop_stride, const void* w, int32_t dtype, const float* bias,
                         const void* seeds, int32_t seed_dtype, int64_t pop, int64_t batch, int64_t in, int64_t out,
-                        float sigma, int64_t offset, int32_t activation, int32_t math, float* y,
-                        void* stream) {
+                        float sigma, int64_t offset, int32_t activation, int32_t math, float* y, void* workspace,
+                        int64_t workspace_bytes, void* stream) {
   bool i32 = false;
   if (dtype != VN_F32 && dtype != VN_BF16) return VN_ERR_DTYPE;
   int st = seed_kind(seed_dtype, &i32);
@@ -148,6 +162,8 @@ int vn_perturbed_linear(const void* x, int64_t x_pop_stride, const void* w, int3
   if (!aligned(x, esz) || !aligned(w, esz) || !aligned(y, 4) || !aligned(bias, 4) ||
       !aligned(seeds, i32 ? 4 : 8))
     return VN_ERR_ALIGN;
+  if (workspace_bytes < 0) return VN_ERR_SHAPE;
+  if (!aligned(workspace, 16)) return VN_ERR_ALIGN;
 
   vn::FwdParams p;
   p.x = x;
@@ -170,8 +186,16 @@ int vn_perturbed_linear(const void* x, int64_t x_pop_stride, const void* w, int3
   // falls below the normal range; such a sigma takes the kernels that form
   // sigma * N in floating point.
   const bool tiny_sigma = sigma != 0.0f && std::fabs(sigma) < 0x1p-100f;
-  if (dtype == VN_BF16)
-    return hip_status(tiny_sigma ? vn::launch_forward_bf16_exact(p, s) : vn::launch_forward_bf16(p, s));
+  if (dtype == VN_BF16) {
+    if (tiny_sigma) return hip_status(vn::launch_forward_bf16_exact(p, s));
+    // Many rows per individual: perturbed weights formed once in the caller's
+    // workspace, then a matrix-core product (the same bits as the fused path).
+    if (workspace != nullptr && vn::materialized_forward_applies(batch, in, out) &&
+        workspace_bytes >= vn::materialized_workspace_bytes(pop, batch, in, out) && aligned(x, 16) && aligned(w, 16) &&
+        x_pop_stride % 8 == 0)
+      return hip_status(vn::launch_forward_bf16_materialized(p, workspace, s));
+    return hip_status(vn::launch_forward_bf16(p, s));
+  }
   return hip_status(math == VN_MATH_F32 || tiny_sigma ? vn::launch_forward_f32_exact(p, s)
                                                        : vn::launch_forward_f32(p, s));
 }

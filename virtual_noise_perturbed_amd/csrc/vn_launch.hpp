@@ -83,4 +83,35 @@ hipError_t metric_scratch_address(float** ptr);
 // Largest grid.x the launchers use (they loop inside the kernel beyond it).
 constexpr int64_t kMaxGridX = 0x7FFFFFFF;
 
+// Large-batch bf16 forward through materialized perturbed weights (vn_gemm.hip).
+constexpr int64_t kMaterializeMinBatch = 2048;          // rows per individual from which it is used
+constexpr int64_t kMaterializeBytes = int64_t{1} << 28; // workspace budget: individuals per group
+constexpr int64_t kMatmulGrid = 256;                    // persistent workgroups (one per CU)
+struct MatParams {
+  const __bf16* x;
+  int64_t x_pop_stride;
+  const __bf16* wp;       // perturbed weights of the group, (group, out, in)
+  int64_t wp_stride;      // out * in
+  const float* bias;      // may be null
+  const void* seeds;
+  bool seeds_i32;
+  float sigma;
+  int64_t offset;
+  bool relu;
+  float* y;
+  int64_t i0;             // first individual of the group
+  int64_t total_tiles;    // group size * tiles_m * tiles_n
+  int64_t m, n, k;        // batch, out, in
+  int32_t tiles_m, tiles_n;
+};
+// Shapes the materialized path takes: batch >= kMaterializeMinBatch,
+// in a multiple of 64 in [128, 2^22), and fewer than 2^31 tiles per individual.
+bool materialized_forward_applies(int64_t batch, int64_t in, int64_t out);
+// Individuals per group and the workspace bytes the path needs.
+int64_t materialized_group(int64_t pop, int64_t batch, int64_t in, int64_t out);
+int64_t materialized_workspace_bytes(int64_t pop, int64_t batch, int64_t in, int64_t out);
+// x, w 16-byte aligned, x_pop_stride a multiple of 8, workspace 16-byte
+// aligned with materialized_workspace_bytes.
+hipError_t launch_forward_bf16_materialized(const FwdParams& p, void* workspace, hipStream_t stream);
+
 }  // namespace vn
