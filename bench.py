@@ -409,6 +409,8 @@ def cpu_baseline(wl, budget_s: float, max_procs: int = 16):
                    f"{m // chunk} runs of {chunk} flat elements at random starts (of {total}) over all "
                    f"{wl.pop} individuals ({t_grad:.1f} s wall), scaled to one step ({est_step:.2f} s)"),
         "step_s_estimate": est_step,
+        "forward_s_per_step": fwd_per_indiv * wl.pop,
+        "gradient_s_per_step": grad_per_elem * total,
         "grad_elements_per_s": wl.pop * m / t_grad,
     }
 
