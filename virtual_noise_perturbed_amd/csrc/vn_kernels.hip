@@ -70,17 +70,18 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t n) {
 
 // (individual, column tile) of workgroup b when every individual has its own
 // X and several column tiles.  Each XCD takes a contiguous range of the
-// logical order (xcd_remap), which walks groups of 8 individuals x all tiles,
-// within a group blocks of 8 tiles, individual fastest inside a block.  The
-// 64 workgroups an XCD runs at once thus share 8 individuals' X rows and 8
-// tiles of W in its L2: on the 4096 -> 4096 bf16 projection (pop 128,
-// batch 256, 16 tiles) reads beyond L2 fell from 2.42 GB to 1.61 GB per launch
-// against an order that ran each individual's tiles back to back on one XCD,
-// in the same time.  A bijection on [0, pop * n_tiles) (the last group and
-// block may be smaller).
+// logical order (xcd_remap), which walks groups of IG individuals x all tiles,
+// within a group blocks of TG tiles, individual fastest inside a block, with
+// TG = min(n_tiles, 8) and IG = 64 / TG: the 64 workgroups an XCD runs at once
+// share IG individuals' X rows and TG tiles of W in its L2.  On the
+// 4096 -> 4096 bf16 projection (pop 128, batch 256, 16 tiles) reads beyond L2
+// fell from 2.42 GB to 1.61 GB per launch against an order that ran each
+// individual's tiles back to back on one XCD, in the same time.  A bijection
+// on [0, pop * n_tiles) (the last group and block may be smaller).
 __device__ __forceinline__ void blocked_order(int64_t b, int64_t n, int64_t pop, int64_t n_tiles, int64_t& i,
                                               int64_t& tile) {
-  constexpr int64_t IG = 8, TG = 8;
+  const int64_t TG = n_tiles < 8 ? n_tiles : 8;
+  const int64_t IG = 64 / TG;
   const int64_t L = xcd_remap(b, n);
   const int64_t ig = L / (IG * n_tiles);
   const int64_t igs = (pop - ig * IG) < IG ? (pop - ig * IG) : IG;   // individuals in this group
