@@ -68,3 +68,50 @@ def test_graph_replays_match_eager():
         for got, exp, name in zip((h, y, grad), want, ("hidden", "output", "gradient")):
             assert torch.equal(got, exp), f"replay {r}: {name}"
     assert not np.array_equal(want[2].cpu().numpy(), np.zeros(n, dtype=np.float32))
+
+
+def test_graph_replays_match_eager_large_batch():
+    """The large-batch bf16 forward (perturbed weights formed in a workspace the
+    binding allocates, two groups of individuals, so four kernels per call) and
+    the reduce metric, captured together: replays equal eager calls."""
+    print("graph capture: materialized large-batch forward + reduce metric", flush=True)
+    dev = device()
+    g = torch.Generator().manual_seed(11)
+    pop, batch, fin, fout = 9, 2048, 4096, 4096          # 8 individuals per 256 MiB group
+    x = torch.randn(batch, fin, generator=g).to(torch.bfloat16).to(dev)
+    w = (torch.randn(fout, fin, generator=g) / 64).to(torch.bfloat16).to(dev)
+    b = torch.randn(fout, generator=g).to(dev)
+    seeds = (torch.arange(pop) * 7919 + 3).to(dev)
+    center = torch.randn(fout * fin, generator=g).to(dev)
+    y = torch.empty(pop, batch, fout, device=dev)
+    res = {}
+    sigma = 0.01
+
+    def step():
+        vn.virtual_perturbed_linear(x, w, b, seeds, sigma, 17, out=y)
+        res["met"] = vn.virtual_reduce_metric(center, seeds, sigma, fout * fin, 17)
+
+    def eager():
+        step()
+        torch.cuda.synchronize()
+        return y.clone(), res["met"].clone()
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    want = eager()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    met = res["met"]                            # the graph's own output of the metric
+    for r in range(3):
+        y.zero_(), met.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _ = (torch.ones(1000, device=dev) * r).sum().item()    # eager work between replays
+        assert torch.equal(y, want[0]), f"replay {r}: output"
+        assert torch.equal(met, want[1]), f"replay {r}: metric"
