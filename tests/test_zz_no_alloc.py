@@ -53,3 +53,35 @@ def test_noalloc_without_partial_sums():
     ref = vn.virtual_reduce_metric(c, s, 0.5, 4099, offset)
     torch.cuda.synchronize()
     assert torch.equal(got, ref)
+
+
+def test_noalloc_under_graph_capture():
+    """The callers it is for: a graph captured around the allocation-free call
+    (output given, so the call allocates nothing) replays to the bits of the
+    workspace entry point, with other calls on the same GPU in between that use
+    the fixed array for a different shape."""
+    dev = device()
+    pop, n, offset = 5, 600_001, 9
+    print(f"no-alloc reduce metric under graph capture: pop={pop} n={n}", flush=True)
+    center, seeds, _ = _case(pop, n, offset, seed=21)
+    c, s = to_dev(center), to_dev(seeds)
+    out = torch.empty((pop,), dtype=torch.float32, device=dev)
+    ref = vn.virtual_reduce_metric(c, s, 0.125, n, offset)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):                 # warm-up off the capture stream
+        vn.virtual_reduce_metric_noalloc(c, s, 0.125, n, offset, out=out)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        vn.virtual_reduce_metric_noalloc(c, s, 0.125, n, offset, out=out)
+    c2, s2 = to_dev(_case(3, 70_001, 0, seed=4)[0]), to_dev(_case(3, 70_001, 0, seed=4)[1])
+    for r in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {r}"
+        vn.virtual_reduce_metric_noalloc(c2, s2, 0.5, 70_001, 0)   # another shape through the array
+        torch.cuda.synchronize()
