@@ -72,8 +72,9 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t n) {
 // X and several column tiles.  Each XCD takes a contiguous range of the
 // logical order (xcd_remap), which walks groups of IG individuals x all tiles,
 // within a group blocks of TG tiles, individual fastest inside a block, with
-// TG = min(n_tiles, 8) and IG = 64 / TG: the 64 workgroups an XCD runs at once
-// share IG individuals' X rows and TG tiles of W in its L2.  On the
+// TG = min(n_tiles, 8) and IG = 64 / TG: a block of 64 consecutive workgroups
+// of an XCD (one round of its 32 CUs at two workgroups per CU, two rounds at
+// one) shares IG individuals' X rows and TG tiles of W in its L2.  On the
 // 4096 -> 4096 bf16 projection (pop 128, batch 256, 16 tiles) reads beyond L2
 // fell from 2.42 GB to 1.61 GB per launch against an order that ran each
 // individual's tiles back to back on one XCD, in the same time.  A bijection
