@@ -25,9 +25,11 @@
  *
  * Conventions for every entry point below:
  *  - All pointers except those of vn_compute_offsets are DEVICE pointers owned
- *    by the caller.  The library keeps no state and allocates no memory: the
- *    entry points that use scratch space (vn_reduce_metric, and
- *    vn_perturbed_linear for large batches) take it from the caller.
+ *    by the caller.  The library keeps no state between calls and allocates
+ *    no memory: the entry points that use scratch space (vn_reduce_metric, and
+ *    vn_perturbed_linear for large batches) take it from the caller; the one
+ *    exception, vn_reduce_metric_noalloc, uses a fixed device array described
+ *    at its declaration.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = null stream).
  *    VN_OK means "validated and enqueued"; outputs are valid once the stream
  *    reaches the launch.  Arguments are validated before any HIP call and a
