@@ -33,8 +33,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"p{c[0]}b{c[1]}i{c[2]}o{c[3]}" for c in CASES])
-def test_materialized_same_bits_as_fused(case):
+def _check_same_bits(case):
     pop, batch, fin, fout, bias, shared, relu, s32, offset = case
     print(f"materialized vs fused {case}", flush=True)
     assert _ws_bytes(pop, batch, fin, fout) > 0, "shape should take the materialized path"
@@ -49,6 +48,11 @@ def test_materialized_same_bits_as_fused(case):
     yf = vn.virtual_perturbed_linear(*args, activation=act, materialize=False)
     torch.cuda.synchronize()
     assert torch.equal(ym, yf), f"max |diff| {(ym - yf).abs().max().item():.3e}"
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"p{c[0]}b{c[1]}i{c[2]}o{c[3]}" for c in CASES])
+def test_materialized_same_bits_as_fused(case):
+    _check_same_bits(case)
 
 
 def test_materialized_against_oracle():
@@ -81,3 +85,27 @@ def test_materialized_several_groups():
     yf = vn.virtual_perturbed_linear(x, w, b, seeds, 0.05, 99, materialize=False)
     torch.cuda.synchronize()
     assert torch.equal(ym, yf), f"max |diff| {(ym - yf).abs().max().item():.3e}"
+
+
+def _random_cases(n, seed=2026):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        pop = int(rng.integers(1, 4))
+        batch = int(rng.integers(2048, 2700))
+        fin = int(rng.integers(2, 12)) * 64
+        fout = int(rng.integers(1, 700))
+        cases.append((pop, batch, fin, fout, bool(rng.integers(2)), bool(rng.integers(2)),
+                      bool(rng.integers(2)), bool(rng.integers(2)), int(rng.integers(0, 2**40))))
+    return cases
+
+
+RANDOM_CASES = _random_cases(8)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[f"r{k}" for k in range(len(RANDOM_CASES))])
+def test_materialized_random_shapes_same_bits(case):
+    """Seeded random shapes (ragged batch and out, any in that is a multiple of
+    64, bias / relu / shared x / int32 seeds at random): same bits as the fused
+    kernels."""
+    _check_same_bits(case)
