@@ -138,3 +138,23 @@ def test_bf16_projection_noise_visible(key):
     got = y[torch.as_tensor(ii), torch.as_tensor(bb), torch.as_tensor(jj)].cpu().numpy()
     err = assert_close(got, ref, TOL_BF16, f"workload {key} at sigma {sigma} (noise term {term:.2f})")
     print(f"workload {key}: noise term {term:.3f}, error {err:.2e}", flush=True)
+
+
+def test_reduce_metric_full_size_sampled():
+    """The reduce metric at the wide workload's size (pop 128, n = 4096 * 4096
+    parameters: eight segments per individual, the launch the bench times),
+    sampled: the oracle computes three whole individuals (first, middle,
+    last).  At sigma = 0.5 the noise moves each mean by about 1%, twenty times
+    the tolerance (asserted against the mean without noise)."""
+    dev = device()
+    pop, n, offset, sig = 128, FIN * FOUT, 3, 0.5
+    print(f"reduce metric full size: pop={pop} n={n}", flush=True)
+    rng = np.random.default_rng(20261202 + 5)
+    center = rng.standard_normal(n, dtype=np.float32)
+    seeds = np.arange(pop, dtype=np.int64)
+    got = vn.virtual_reduce_metric(to_dev(center), to_dev(seeds), sig, n, offset).cpu().numpy()
+    pick = np.array([0, 63, 127])
+    want = oracle.reduce_metric(center, seeds[pick], sigma32(sig), n, offset)
+    plain = np.full(len(pick), np.mean(np.abs(center.astype(np.float64))))
+    assert normwise_err(want, plain) > 20 * 1e-4, "the noise must move the means"
+    assert_close(got[pick], want, 1e-4, "reduce metric, sampled individuals")
