@@ -140,20 +140,22 @@ def test_bf16_projection_noise_visible(key):
     print(f"workload {key}: noise term {term:.3f}, error {err:.2e}", flush=True)
 
 
-def test_reduce_metric_full_size_sampled():
-    """The reduce metric at the wide workload's size (pop 128, n = 4096 * 4096
-    parameters: eight segments per individual, the launch the bench times),
-    sampled: the oracle computes three whole individuals (first, middle,
-    last).  At sigma = 0.5 the noise moves each mean by about 1%, twenty times
-    the tolerance (asserted against the mean without noise)."""
-    dev = device()
-    pop, n, offset, sig = 128, FIN * FOUT, 3, 0.5
+@pytest.mark.parametrize("pop", [128, 16])
+def test_reduce_metric_full_size_sampled(pop):
+    """The reduce metric at the sizes of the two bf16 projections (4096 * 4096
+    parameters; pop 128: eight segments per individual, pop 16: 64 -- the
+    launches the bench times), sampled: the oracle computes three whole
+    individuals (first, middle, last).  At sigma = 0.5 the noise moves each
+    mean by about 1%, twenty times the tolerance (asserted against the mean
+    without noise)."""
+    device()
+    n, offset, sig = FIN * FOUT, 3, 0.5
     print(f"reduce metric full size: pop={pop} n={n}", flush=True)
     rng = np.random.default_rng(20261202 + 5)
     center = rng.standard_normal(n, dtype=np.float32)
     seeds = np.arange(pop, dtype=np.int64)
     got = vn.virtual_reduce_metric(to_dev(center), to_dev(seeds), sig, n, offset).cpu().numpy()
-    pick = np.array([0, 63, 127])
+    pick = np.array([0, pop // 2 - 1, pop - 1])
     want = oracle.reduce_metric(center, seeds[pick], sigma32(sig), n, offset)
     plain = np.full(len(pick), np.mean(np.abs(center.astype(np.float64))))
     assert normwise_err(want, plain) > 20 * 1e-4, "the noise must move the means"
