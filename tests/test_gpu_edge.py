@@ -122,6 +122,33 @@ def test_sigma_zero_is_plain_linear():
     assert_close(y.cpu().numpy(), ref, TOL_F32, "sigma 0")
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_negative_sigma(dt):
+    """sigma < 0 is a valid perturbation scale: the forward adds sigma * N, the
+    gradients divide by P * sigma (a negative scale) and the reduce metric
+    takes |c + sigma * N|; everything against the oracle at sigma = -0.3."""
+    print(f"negative sigma {dt}", flush=True)
+    pop, batch, fin, fout, offset = 5, 40, 96, 70, 11
+    wl = workloads.make_custom(pop, batch, fin, fout, dtype=dt, bias=True, sigma=-0.3, offset=offset, seed=31)
+    L = wl.layers[0]
+    tol = TOL_BF16 if dt == "bf16" else TOL_F32
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    sig = sigma32(wl.sigma)
+    seeds = to_dev(wl.seeds)
+    y = vn.virtual_perturbed_linear(to_dev(wl.x, tdt), to_dev(L.weight, tdt), to_dev(L.bias), seeds, wl.sigma,
+                                    offset).cpu().numpy()
+    assert_close(y, oracle.perturbed_linear(wl.x, L.weight, L.bias, wl.seeds, sig, offset), tol, "forward")
+    fit = to_dev(wl.fitness)
+    f64 = wl.fitness.astype(np.float64)
+    gw = vn.virtual_weight_gradient(fit, seeds, (fout, fin), wl.sigma, pop, offset).cpu().numpy()
+    assert_close(gw, oracle.weight_gradient(f64, wl.seeds, (fout, fin), sig, pop, offset), TOL_F32, "grad W")
+    gb = vn.virtual_bias_gradient(fit, seeds, (fout,), wl.sigma, pop, offset + fout * fin).cpu().numpy()
+    assert_close(gb, oracle.bias_gradient(f64, wl.seeds, (fout,), sig, pop, offset + fout * fin), TOL_F32, "grad b")
+    center = np.random.default_rng(3).standard_normal(5000).astype(np.float32)
+    m = vn.virtual_reduce_metric(to_dev(center), seeds, wl.sigma, 5000, offset).cpu().numpy()
+    assert_close(m, oracle.reduce_metric(center, wl.seeds, sig, 5000, offset), TOL_F32, "reduce metric")
+
+
 def test_degenerate_sizes():
     dev = device()
     s = to_dev(np.arange(3, dtype=np.int64))
