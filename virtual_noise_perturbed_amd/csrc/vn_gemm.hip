@@ -24,9 +24,13 @@
 // stages of 64 through two LDS slots (A: 256 rows x 64 k of X, B: 256 rows x
 // 64 k of Wp, 64 KB per slot), filled by direct global->LDS loads issued two
 // stages ahead; the last two stages of a tile load the first two of the next
-// tile, so consecutive tiles overlap.  The loads are issued through inline asm
-// and every wait on them is explicit (vmcnt before the barrier that publishes
-// a stage); the compiler neither tracks nor waits on them.
+// tile, so consecutive tiles overlap.  A stage's 64 loads per workgroup are
+// spread one per two MFMAs over two k-steps (the X half in the k-step that
+// frees the slot, the Wp half in the next), and the MFMA fragments of the
+// next k-step are read one per MFMA, so that neither the address unit's queue
+// nor the LDS sees a burst.  The loads are issued through inline asm and every
+// wait on them is explicit (vmcnt before the barrier that publishes a stage);
+// the compiler neither tracks nor waits on them.
 #include <stdint.h>
 
 #include <utility>
@@ -95,13 +99,14 @@ constexpr int UNITS = BM * 8;   // 16-byte units per operand per stage (256 rows
 // one segment) free of bank conflicts for 8 or 16 lanes per LDS cycle.
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// 16 bytes at g -> LDS byte address base + IMM + 16 * lane (base wave-uniform).
+// 16 bytes at sbase + voff (a wave-uniform 64-bit base, a 32-bit per-lane
+// offset) -> LDS byte address base + IMM + 16 * lane (base wave-uniform).
 // M0 takes the LDS address; one wait state separates its write from the load.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 template <int IMM>
-__device__ __forceinline__ void lds_load16(const void* g, uint32_t base) {
-  asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base), "n"(IMM)
+__device__ __forceinline__ void lds_load16(uint32_t voff, const void* sbase, uint32_t base) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(base), "n"(IMM)
                : "memory", "m0", "scc");
 }
 #pragma clang diagnostic pop
@@ -174,10 +179,10 @@ __global__ __launch_bounds__(256, 1) void matmul_kernel(MatParams g) {
     const int row = lrow + 32 * (u & 7);
     if constexpr (u < 8) {
       const int rr = row < alim ? row : alim;
-      lds_load16<u * 256 * 16>(abase + (static_cast<uint32_t>(rr) * K2 + lseg16 + kb), sa);
+      lds_load16<u * 256 * 16>(static_cast<uint32_t>(rr) * K2 + lseg16, abase + kb, sa);
     } else {
       const int rr = row < blim ? row : blim;
-      lds_load16<UNITS * 16 + (u - 8) * 256 * 16>(bbase + (static_cast<uint32_t>(rr) * K2 + lseg16 + kb), sa);
+      lds_load16<UNITS * 16 + (u - 8) * 256 * 16>(static_cast<uint32_t>(rr) * K2 + lseg16, bbase + kb, sa);
     }
   };
   auto load_stage = [&](const Tile& r, int slot, int64_t k0) {
@@ -213,9 +218,15 @@ __global__ __launch_bounds__(256, 1) void matmul_kernel(MatParams g) {
   else nxt = cur;
   const int64_t klast = (nk - 1) * BK;
 
+  // The Wp half of a stage's loads, deferred to the next k-step 0: Wp rows
+  // at pb, row limit pbl, k offset pkn, into slot pslot (stage 1's here).
+  const char* pb = cur.b;
+  int32_t pbl = cur.blim;
+  int64_t pkn = BK;
+  int pslot = 1;
   load_stage(cur, 0, 0);
-  load_stage(cur, 1, BK);
-  wait_vm<16>();
+  static_for<8>([&](auto uc) { load_u(cur.a, cur.b, cur.alim, cur.blim, 1, BK, uc); });
+  wait_vm<8>();
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < 8; ++q) read_one(0, 0, 0, q);
@@ -227,24 +238,34 @@ __global__ __launch_bounds__(256, 1) void matmul_kernel(MatParams g) {
       for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
     for (int64_t c = 0; c < nk; ++c) {
       const int slot = (par + static_cast<int>(c)) & 1;
-      // k-steps 0..2: fragments of the next k-step, then 16 MFMAs
-#pragma unroll
-      for (int tt = 0; tt < 3; ++tt) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) read_one(slot, tt + 1, (tt + 1) & 1, q);
-#pragma unroll
-        for (int m = 0; m < 16; ++m) mfma1(m, tt & 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-        __builtin_amdgcn_sched_barrier(0);
+      // k-step 0: the fragments of k-step 1 and the deferred Wp loads between
+      // the MFMAs; k-steps 1 and 2: the fragments of the next k-step.
+      {
+        static_for<16>([&](auto mc) {
+          constexpr int m = decltype(mc)::value;
+          mfma1(m, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (m < 8) read_one(slot, 1, 1, m);
+          if constexpr (m % 2 == 0) load_u(pb, pb, pbl, pbl, pslot, pkn, std::integral_constant<int, 8 + m / 2>{});
+          __builtin_amdgcn_sched_barrier(0);
+        });
       }
-      // k-step 3: after two MFMAs, wait for stage c+1 and the barrier that
-      // publishes it and frees this slot (every wave holds its fragments);
-      // then the loads of stage c+2 (this tile's, else the next tile's stage
-      // c+2-nk, else an unused in-bounds reload) and the fragments of stage
-      // c+1's k-step 0 go between the remaining MFMAs.
-      mfma1(0, 1);
-      mfma1(1, 1);
+      static_for<2>([&](auto tc) {
+        constexpr int tt = decltype(tc)::value + 1;
+        static_for<16>([&](auto mc) {
+          constexpr int m = decltype(mc)::value;
+          mfma1(m, tt & 1);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (m < 8) read_one(slot, tt + 1, (tt + 1) & 1, m);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      });
+      // k-step 3: wait for stage c+1 and the barrier that publishes it and
+      // frees this slot (every wave holds this k-step's fragments); then the X
+      // loads of stage c+2 (this tile's, else the next tile's stage c+2-nk,
+      // else an unused in-bounds reload) and the fragments of stage c+1's
+      // k-step 0 go between the MFMAs, and stage c+2's Wp loads wait for the
+      // next k-step 0.
       __builtin_amdgcn_sched_barrier(0);
       wait_vm<0>();
       __syncthreads();
@@ -255,19 +276,18 @@ __global__ __launch_bounds__(256, 1) void matmul_kernel(MatParams g) {
       const char* sb_ = nx ? nxt.b : cur.b;
       const int32_t al = nx ? nxt.alim : cur.alim, bl = nx ? nxt.blim : cur.blim;
       const int64_t kn = own ? (c + 2) * BK : (nx ? (c + 2 - nk) * BK : klast);
-      static_for<14>([&](auto mc) {
-        constexpr int m = decltype(mc)::value + 2;
+      static_for<16>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
         mfma1(m, 1);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (m < 10) {
-          load_u(sa_, sb_, al, bl, slot, kn, std::integral_constant<int, 2 * (m - 2)>{});
-          load_u(sa_, sb_, al, bl, slot, kn, std::integral_constant<int, 2 * (m - 2) + 1>{});
-        } else if constexpr (m < 14) {
-          read_one(slot ^ 1, 0, 0, 2 * (m - 10));
-          read_one(slot ^ 1, 0, 0, 2 * (m - 10) + 1);
-        }
+        if constexpr (m % 2 == 0) load_u(sa_, sb_, al, bl, slot, kn, std::integral_constant<int, m / 2>{});
+        if constexpr (m >= 1 && m <= 8) read_one(slot ^ 1, 0, 0, m - 1);
         __builtin_amdgcn_sched_barrier(0);
       });
+      pb = sb_;
+      pbl = bl;
+      pkn = kn;
+      pslot = slot;
     }
 
     // Epilogue: bias b_j + sigma nb_i[j] with nb at offset + out*in + j.
