@@ -156,8 +156,8 @@ int vn_perturbed_linear(const void* x, int64_t x_pop_stride, const void* w, int3
 /*
  * Device workspace, in bytes, with which vn_perturbed_linear takes its
  * materialized-weights path for these sizes; 0 when the sizes do not take it
- * (fp32 operands, fewer than 2048 rows per individual, in not a multiple of 64
- * in [128, 2^22)).  At most 256 MiB, or one individual's out*in bf16 values
+ * (fp32 operands, fewer than 2048 rows per individual, fewer than 256 outputs,
+ * in not a multiple of 64 in [128, 2^22)).  At most 256 MiB, or one individual's out*in bf16 values
  * when that is larger.  Errors: VN_ERR_NULL (bytes_out), VN_ERR_DTYPE,
  * VN_ERR_SHAPE (negative size), VN_ERR_VALUE (math), VN_ERR_OVERFLOW.
  */

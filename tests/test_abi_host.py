@@ -279,7 +279,8 @@ def test_forward_workspace_size(lib):
     assert ws_size(lib, E.VN_BF16, 16, 4096, 4096, 4096) == (E.VN_OK, 8 * 32 * mib)
     assert ws_size(lib, E.VN_BF16, 3, 2048, 4096, 4096) == (E.VN_OK, 3 * 32 * mib)
     assert ws_size(lib, E.VN_BF16, 2, 2048, 16384, 16384) == (E.VN_OK, 512 * mib)   # one individual per group
-    assert ws_size(lib, E.VN_BF16, 1, 2048, 128, 1) == (E.VN_OK, 256)
+    assert ws_size(lib, E.VN_BF16, 1, 2048, 128, 256) == (E.VN_OK, 256 * 128 * 2)
+    assert ws_size(lib, E.VN_BF16, 1, 2048, 128, 255) == (E.VN_OK, 0)       # fewer than 256 outputs
     # sizes that keep the noise inside the product: no workspace
     assert ws_size(lib, E.VN_F32, 16, 4096, 4096, 4096) == (E.VN_OK, 0)
     assert ws_size(lib, E.VN_BF16, 16, 2047, 4096, 4096) == (E.VN_OK, 0)

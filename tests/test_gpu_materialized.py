@@ -28,7 +28,7 @@ CASES = [
     (3, 2048, 256, 384, True, False, True, False, 7),       # ragged column tile, bias + relu
     (2, 2100, 192, 256, False, True, False, False, 2**33),  # ragged row tile, shared x
     (2, 2304, 128, 300, True, True, False, True, 3),        # two k-stages only; int32 seeds
-    (1, 2048, 640, 100, True, False, True, False, 0),       # one ragged tile narrower than 256
+    (1, 2048, 640, 257, True, False, True, False, 0),       # last column tile of one column, moved back
     (4, 2560, 320, 512, False, False, False, False, 11),    # odd number of k-stages (5)
 ]
 
@@ -55,9 +55,12 @@ def test_materialized_same_bits_as_fused(case):
     _check_same_bits(case)
 
 
-def test_materialized_against_oracle():
-    pop, batch, fin, fout, offset = 2, 2048, 128, 272, 5
-    print("materialized vs oracle", flush=True)
+@pytest.mark.parametrize("pop,batch,fin,fout,offset", [
+    (2, 2048, 128, 272, 5),      # ragged last column tile (moved back by 240 columns)
+    (1, 2100, 192, 300, 2**35),  # ragged last row tile and column tile
+])
+def test_materialized_against_oracle(pop, batch, fin, fout, offset):
+    print(f"materialized vs oracle {(pop, batch, fin, fout, offset)}", flush=True)
     assert _ws_bytes(pop, batch, fin, fout) > 0
     wl = workloads.make_custom(pop, batch, fin, fout, dtype="bf16", bias=True, shared_x=False, sigma=0.05,
                                offset=offset, seed=44)
@@ -94,7 +97,7 @@ def _random_cases(n, seed=2026):
         pop = int(rng.integers(1, 4))
         batch = int(rng.integers(2048, 2700))
         fin = int(rng.integers(2, 12)) * 64
-        fout = int(rng.integers(1, 700))
+        fout = int(rng.integers(256, 700))
         cases.append((pop, batch, fin, fout, bool(rng.integers(2)), bool(rng.integers(2)),
                       bool(rng.integers(2)), bool(rng.integers(2)), int(rng.integers(0, 2**40))))
     return cases

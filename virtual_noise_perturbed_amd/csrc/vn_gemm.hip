@@ -30,7 +30,11 @@
 // next k-step are read one per MFMA, so that neither the address unit's queue
 // nor the LDS sees a burst.  The loads are issued through inline asm and every
 // wait on them is explicit (vmcnt before the barrier that publishes a stage);
-// the compiler neither tracks nor waits on them.
+// the compiler neither tracks nor waits on them.  A ragged last row or column
+// tile is moved back to end at the last row or column (batch and out are at
+// least 256 here), so every load reads 256 valid rows and the per-lane load
+// offsets are the same for every tile; the outputs that the previous tile
+// owns are recomputed and not stored.
 #include <stdint.h>
 
 #include <utility>
@@ -125,11 +129,13 @@ __device__ __forceinline__ void wait_vm() {
 
 // One tile's operand sources: tile-relative row limits clamp the loads of a
 // ragged last tile to its last valid row (those rows feed discarded outputs).
+// One tile's operand sources.  The tile owns output rows [m0, m0 + 256) and
+// columns [n0, n0 + 256) (cut at batch and out); it computes rows from me and
+// columns from ne, which differ from m0 and n0 only for a ragged last tile.
 struct Tile {
-  const char* a;      // X rows of the tile (byte address of row m0, k 0)
-  const char* b;      // Wp rows of the tile
-  int32_t alim, blim; // last valid row of each, capped at 256
-  int64_t i, m0, n0;
+  const char* a;   // X rows of the tile (byte address of row me, k 0)
+  const char* b;   // Wp rows of the tile (row ne)
+  int64_t i, m0, n0, me, ne;
 };
 
 __global__ __launch_bounds__(256, 1) void matmul_kernel(MatParams g) {
@@ -160,33 +166,32 @@ __global__ __launch_bounds__(256, 1) void matmul_kernel(MatParams g) {
     r.i = g.i0 + il;
     r.m0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(first + r2 % gsz)) * BM;
     r.n0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(r2 / gsz)) * BN;
-    r.a = reinterpret_cast<const char*>(g.x + r.i * g.x_pop_stride + r.m0 * K);
-    r.b = reinterpret_cast<const char*>(g.wp + il * g.wp_stride + r.n0 * K);
-    const int64_t am = g.m - 1 - r.m0, bm = g.n - 1 - r.n0;
-    r.alim = static_cast<int32_t>(am < BM ? am : BM);
-    r.blim = static_cast<int32_t>(bm < BN ? bm : BN);
+    r.me = r.m0 + BM <= g.m ? r.m0 : g.m - BM;
+    r.ne = r.n0 + BN <= g.n ? r.n0 : g.n - BN;
+    r.a = reinterpret_cast<const char*>(g.x + r.i * g.x_pop_stride + r.me * K);
+    r.b = reinterpret_cast<const char*>(g.wp + il * g.wp_stride + r.ne * K);
   };
 
   // Load u of a stage (u < 8: A, else B) fills unit (u % 8) * 256 + tid of its
-  // operand: row (u % 8) * 32 + tid / 8, k-segment (tid % 8) ^ swz(row).
+  // operand: row (u % 8) * 32 + tid / 8, k-segment (tid % 8) ^ swz(row), at a
+  // per-lane offset voff[u % 8] from the operand's row 0 at the stage's k.
   const int lrow = tid >> 3;
   const uint32_t lseg16 = static_cast<uint32_t>(((tid & 7) ^ swz(lrow)) * 16);
   const uint32_t wave_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem)) + wave * 64 * 16;
-  auto load_u = [&](const char* abase, const char* bbase, int32_t alim, int32_t blim, int slot, int64_t k0, auto uc) {
+  uint32_t voff[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) voff[u] = static_cast<uint32_t>(lrow + 32 * u) * K2 + lseg16;
+  auto load_u = [&](const char* abase, const char* bbase, int slot, int64_t k0, auto uc) {
     constexpr int u = decltype(uc)::value;
     const uint32_t kb = static_cast<uint32_t>(k0 * 2);
     const uint32_t sa = __builtin_amdgcn_readfirstlane(wave_lds + slot * (2 * UNITS * 16));
-    const int row = lrow + 32 * (u & 7);
-    if constexpr (u < 8) {
-      const int rr = row < alim ? row : alim;
-      lds_load16<u * 256 * 16>(static_cast<uint32_t>(rr) * K2 + lseg16, abase + kb, sa);
-    } else {
-      const int rr = row < blim ? row : blim;
-      lds_load16<UNITS * 16 + (u - 8) * 256 * 16>(static_cast<uint32_t>(rr) * K2 + lseg16, bbase + kb, sa);
-    }
+    if constexpr (u < 8)
+      lds_load16<u * 256 * 16>(voff[u], abase + kb, sa);
+    else
+      lds_load16<UNITS * 16 + (u - 8) * 256 * 16>(voff[u - 8], bbase + kb, sa);
   };
   auto load_stage = [&](const Tile& r, int slot, int64_t k0) {
-    static_for<16>([&](auto uc) { load_u(r.a, r.b, r.alim, r.blim, slot, k0, uc); });
+    static_for<16>([&](auto uc) { load_u(r.a, r.b, slot, k0, uc); });
   };
 
   // MFMA fragments: lane l reads row (or column) l % 32 of a 32-block at
@@ -221,11 +226,10 @@ __global__ __launch_bounds__(256, 1) void matmul_kernel(MatParams g) {
   // The Wp half of a stage's loads, deferred to the next k-step 0: Wp rows
   // at pb, row limit pbl, k offset pkn, into slot pslot (stage 1's here).
   const char* pb = cur.b;
-  int32_t pbl = cur.blim;
   int64_t pkn = BK;
   int pslot = 1;
   load_stage(cur, 0, 0);
-  static_for<8>([&](auto uc) { load_u(cur.a, cur.b, cur.alim, cur.blim, 1, BK, uc); });
+  static_for<8>([&](auto uc) { load_u(cur.a, cur.b, 1, BK, uc); });
   wait_vm<8>();
   __syncthreads();
 #pragma unroll
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(256, 1) void matmul_kernel(MatParams g) {
           mfma1(m, 0);
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (m < 8) read_one(slot, 1, 1, m);
-          if constexpr (m % 2 == 0) load_u(pb, pb, pbl, pbl, pslot, pkn, std::integral_constant<int, 8 + m / 2>{});
+          if constexpr (m % 2 == 0) load_u(pb, pb, pslot, pkn, std::integral_constant<int, 8 + m / 2>{});
           __builtin_amdgcn_sched_barrier(0);
         });
       }
@@ -274,18 +278,16 @@ __global__ __launch_bounds__(256, 1) void matmul_kernel(MatParams g) {
       const bool nx = !own && has_next;
       const char* sa_ = nx ? nxt.a : cur.a;
       const char* sb_ = nx ? nxt.b : cur.b;
-      const int32_t al = nx ? nxt.alim : cur.alim, bl = nx ? nxt.blim : cur.blim;
       const int64_t kn = own ? (c + 2) * BK : (nx ? (c + 2 - nk) * BK : klast);
       static_for<16>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
         mfma1(m, 1);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (m % 2 == 0) load_u(sa_, sb_, al, bl, slot, kn, std::integral_constant<int, m / 2>{});
+        if constexpr (m % 2 == 0) load_u(sa_, sb_, slot, kn, std::integral_constant<int, m / 2>{});
         if constexpr (m >= 1 && m <= 8) read_one(slot ^ 1, 0, 0, m - 1);
         __builtin_amdgcn_sched_barrier(0);
       });
       pb = sb_;
-      pbl = bl;
       pkn = kn;
       pslot = slot;
     }
@@ -302,14 +304,14 @@ __global__ __launch_bounds__(256, 1) void matmul_kernel(MatParams g) {
         const uint64_t s = load_seed(g.seeds, g.seeds_i32, cur.i);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const int64_t j = cur.n0 + wn * 128 + b * 32 + l32;
+          const int64_t j = cur.ne + wn * 128 + b * 32 + l32;
           if (j < g.n) {
             const float nz = noise_of_state(state_of(s, static_cast<uint64_t>(g.offset + g.n * K + j)));
             bj[b] = __builtin_fmaf(g.sigma, nz, g.bias[j]);
           }
         }
       }
-      const bool full = cur.m0 + BM <= g.m && cur.n0 + BN <= g.n;
+      const bool full = cur.me == cur.m0 && cur.ne == cur.n0;
       // the row pitch, opaque here so that the 16 row offsets below are formed
       // per tile rather than held in scalar registers through the k loop
       int64_t pitch = g.n;
@@ -318,17 +320,17 @@ __global__ __launch_bounds__(256, 1) void matmul_kernel(MatParams g) {
 #endif
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int64_t j = cur.n0 + wn * 128 + b * 32 + l32;
+        const int64_t j = cur.ne + wn * 128 + b * 32 + l32;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const int64_t row0 = cur.m0 + wm * 128 + a * 32 + 4 * lh;
+          const int64_t row0 = cur.me + wm * 128 + a * 32 + 4 * lh;
           float* __restrict__ yp = g.y + (cur.i * g.m + row0) * pitch + j;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int ro = 8 * (v >> 2) + (v & 3);
             float val = agpr_read(acc[a][b][v]) + bj[b];
             if (g.relu) val = val > 0.0f ? val : 0.0f;
-            if (full || (j < g.n && row0 + ro < g.m)) yp[static_cast<int64_t>(ro) * pitch] = val;
+            if (full || (j >= cur.n0 && row0 + ro >= cur.m0)) yp[static_cast<int64_t>(ro) * pitch] = val;
           }
         }
       }
@@ -346,8 +348,10 @@ __global__ __launch_bounds__(256, 1) void matmul_kernel(MatParams g) {
 
 }  // namespace
 
+static_assert(kMaterializeMinBatch >= BM, "a ragged last row tile is moved back by up to BM - 1 rows");
+
 bool materialized_forward_applies(int64_t batch, int64_t in, int64_t out) {
-  if (batch < kMaterializeMinBatch || in < 2 * BK || in % BK != 0 || in >= (int64_t{1} << 22) || out < 1 ||
+  if (batch < kMaterializeMinBatch || in < 2 * BK || in % BK != 0 || in >= (int64_t{1} << 22) || out < BN ||
       out >= (int64_t{1} << 26))
     return false;
   const int64_t tm = (batch + BM - 1) / BM, tn = (out + BN - 1) / BN;

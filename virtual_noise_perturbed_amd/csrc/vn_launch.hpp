@@ -105,7 +105,8 @@ struct MatParams {
   int32_t tiles_m, tiles_n;
 };
 // Shapes the materialized path takes: batch >= kMaterializeMinBatch,
-// in a multiple of 64 in [128, 2^22), and fewer than 2^31 tiles per individual.
+// 256 <= out < 2^26, in a multiple of 64 in [128, 2^22), and fewer than 2^31
+// tiles per individual.
 bool materialized_forward_applies(int64_t batch, int64_t in, int64_t out);
 // Individuals per group and the workspace bytes the path needs.
 int64_t materialized_group(int64_t pop, int64_t batch, int64_t in, int64_t out);
