@@ -297,7 +297,9 @@ __global__ __launch_bounds__(256, 1) void matmul_kernel(MatParams g) {
     // 8 * (v / 4) + 4 * (l / 32) + v % 4 for v < 16.  Each accumulator is
     // copied out of its AGPR right before its store, so that no block's copies
     // are held at once.  (Without a bias the epilogue issues no loads: a load
-    // here would wait for the next tile's stage loads too.)
+    // here would wait for the next tile's stage loads too.)  The activation
+    // and the ownership checks of a ragged tile are resolved per tile, so a
+    // full tile's stores carry no per-element branches.
     {
       float bj[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (g.bias != nullptr) {
@@ -312,27 +314,42 @@ __global__ __launch_bounds__(256, 1) void matmul_kernel(MatParams g) {
         }
       }
       const bool full = cur.me == cur.m0 && cur.ne == cur.n0;
-      // the row pitch, opaque here so that the 16 row offsets below are formed
-      // per tile rather than held in scalar registers through the k loop
+      // the row pitch, opaque here so that the row steps below are formed per
+      // tile rather than held in scalar registers through the k loop
       int64_t pitch = g.n;
 #if defined(__HIP_DEVICE_COMPILE__)
       asm volatile("" : "+s"(pitch));
 #endif
+      // A lane's 16 values of a block lie in rows 0-3, 8-11, 16-19, 24-27 of
+      // its 4-row offset: one row step within a group of four, five between.
+      const int64_t step1 = pitch * 4, step5 = pitch * 20;
+      auto store_tile = [&](auto checked, auto relu) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int64_t j = cur.ne + wn * 128 + b * 32 + l32;
+        for (int b = 0; b < 4; ++b) {
+          const int64_t j = cur.ne + wn * 128 + b * 32 + l32;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int64_t row0 = cur.me + wm * 128 + a * 32 + 4 * lh;
-          float* __restrict__ yp = g.y + (cur.i * g.m + row0) * pitch + j;
+          for (int a = 0; a < 4; ++a) {
+            const int64_t row0 = cur.me + wm * 128 + a * 32 + 4 * lh;
+            char* yp = reinterpret_cast<char*>(g.y + (cur.i * g.m + row0) * pitch + j);
+            // ragged tile: this lane stores row0 + ro when ro >= skip (the rows
+            // before m0, or all 32 when the column belongs to the previous tile)
+            const int skip = j < cur.n0 ? 32 : static_cast<int>(cur.m0 - row0 > 0 ? cur.m0 - row0 : 0);
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int ro = 8 * (v >> 2) + (v & 3);
-            float val = agpr_read(acc[a][b][v]) + bj[b];
-            if (g.relu) val = val > 0.0f ? val : 0.0f;
-            if (full || (j >= cur.n0 && row0 + ro >= cur.m0)) yp[static_cast<int64_t>(ro) * pitch] = val;
+            for (int v = 0; v < 16; ++v) {
+              float val = agpr_read(acc[a][b][v]) + bj[b];
+              if constexpr (decltype(relu)::value) val = val > 0.0f ? val : 0.0f;
+              if (!decltype(checked)::value || 8 * (v >> 2) + (v & 3) >= skip) *reinterpret_cast<float*>(yp) = val;
+              yp += (v & 3) == 3 ? step5 : step1;
+            }
           }
         }
+      };
+      if (full) {
+        if (g.relu) store_tile(std::false_type{}, std::true_type{});
+        else store_tile(std::false_type{}, std::false_type{});
+      } else {
+        if (g.relu) store_tile(std::true_type{}, std::true_type{});
+        else store_tile(std::true_type{}, std::false_type{});
       }
     }
     if (!has_next) break;
