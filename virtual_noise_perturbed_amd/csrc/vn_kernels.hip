@@ -129,6 +129,46 @@ template <> struct Mfma<__bf16, 16> : Out16 {  // v_mfma_f32_16x16x32_bf16
   using Acc = f32x4;
 };
 
+// Epilogue of the matrix-core forward kernels: y[r][j[nb]] = act(acc + bj[nb])
+// for a lane's output rows r = rstart + mb * DIMR + MF::row_off(v) (rstart
+// counted from y's row 0; with !FULL, only rows with mb * DIMR + row_off(v) <
+// rleft) and its columns j[nb] < out.  The activation and the row check are
+// compile-time, so a full tile's stores carry no per-element branches, and
+// the address steps from one row to the next instead of being recomputed.
+template <typename MF, int DIMR, bool FULL, bool RELU, int MB, int NB, typename Acc>
+__device__ __forceinline__ void store_rows(float* __restrict__ y, int64_t rstart, int64_t rleft, int64_t out,
+                                           const int64_t (&j)[NB], const float (&bj)[NB], const Acc (&acc)[MB][NB]) {
+  const int64_t step = out * static_cast<int64_t>(sizeof(float));
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    if (j[nb] >= out) continue;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      char* yp = reinterpret_cast<char*>(y + (rstart + mb * DIMR) * out + j[nb]);
+      const int64_t lim = rleft - mb * DIMR;
+#pragma unroll
+      for (int v = 0; v < MF::NACC; ++v) {
+        float val = acc[mb][nb][v] + bj[nb];
+        if constexpr (RELU) val = val > 0.0f ? val : 0.0f;
+        if (FULL || MF::row_off(v) < lim) *reinterpret_cast<float*>(yp) = val;
+        if (v + 1 < MF::NACC) yp += (MF::row_off(v + 1) - MF::row_off(v)) * step;
+      }
+    }
+  }
+}
+template <typename MF, int DIMR, int MB, int NB, typename Acc>
+__device__ __forceinline__ void store_outputs(bool full, bool relu, float* __restrict__ y, int64_t rstart,
+                                              int64_t rleft, int64_t out, const int64_t (&j)[NB],
+                                              const float (&bj)[NB], const Acc (&acc)[MB][NB]) {
+  if (full) {
+    if (relu) store_rows<MF, DIMR, true, true>(y, rstart, rleft, out, j, bj, acc);
+    else store_rows<MF, DIMR, true, false>(y, rstart, rleft, out, j, bj, acc);
+  } else {
+    if (relu) store_rows<MF, DIMR, false, true>(y, rstart, rleft, out, j, bj, acc);
+    else store_rows<MF, DIMR, false, false>(y, rstart, rleft, out, j, bj, acc);
+  }
+}
+
 template <int DIM>
 __device__ __forceinline__ typename Mfma<float, DIM>::Acc mfma_f32(float a, float b, typename Mfma<float, DIM>::Acc c) {
   if constexpr (DIM == 32) return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -285,30 +325,19 @@ __global__ __launch_bounds__(256, WAVES) void forward_kernel(FwdParams p, int64_
 
     // Epilogue: bias b_j + sigma nb_i[j] with nb at offset + out*in + j.
     const int rb = MF::row_base(lane);
+    int64_t jj[NB];
+    float bj[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int64_t j = jbase + nb * DIM + ln;
-      if (j >= out) continue;
-      float bj = 0.0f;
-      if (p.bias != nullptr) {
-        const float nz = noise_of_state(state_of(s, static_cast<uint64_t>(p.offset + out * in + j)));
-        bj = __builtin_fmaf(p.sigma, nz, p.bias[j]);
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int64_t row0 = m0 + mb * DIM + rb;
-        float* __restrict__ yp = p.y + (i * batch + row0) * out + j;
-#pragma unroll
-        for (int v = 0; v < MF::NACC; ++v) {
-          const int ro = MF::row_off(v);
-          if (row0 + ro < batch) {
-            float val = acc[mb][nb][v] + bj;
-            if (p.relu) val = val > 0.0f ? val : 0.0f;
-            yp[static_cast<int64_t>(ro) * out] = val;
-          }
-        }
+      jj[nb] = jbase + nb * DIM + ln;
+      bj[nb] = 0.0f;
+      if (p.bias != nullptr && jj[nb] < out) {
+        const float nz = noise_of_state(state_of(s, static_cast<uint64_t>(p.offset + out * in + jj[nb])));
+        bj[nb] = __builtin_fmaf(p.sigma, nz, p.bias[jj[nb]]);
       }
     }
+    store_outputs<MF, DIM>(m0 + MB * DIM <= batch, p.relu, p.y, i * batch + m0 + rb, batch - (m0 + rb), out, jj, bj,
+                              acc);
   }
 }
 
@@ -653,30 +682,19 @@ __global__ __launch_bounds__(64 * WPG, WAVES) void forward_mm_kernel(FwdParams p
 
   // Epilogue: bias b_j + sigma nb_i[j] with nb at offset + out*in + j.
   const int rb = MF::row_base(lane);
+  int64_t jj[NB];
+  float bj[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int64_t j = jbase + nb * DIM + ln;
-    if (j >= out) continue;
-    float bj = 0.0f;
-    if (p.bias != nullptr) {
-      const float nz = noise_of_state(state_of(s, static_cast<uint64_t>(p.offset + out * in + j)));
-      bj = __builtin_fmaf(p.sigma, nz, p.bias[j]);
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int64_t row0 = m0 + mb * DIM + rb;
-      float* __restrict__ yp = p.y + (i * batch + row0) * out + j;
-#pragma unroll
-      for (int v = 0; v < MF::NACC; ++v) {
-        const int ro = MF::row_off(v);
-        if (row0 + ro < batch) {
-          float val = acc[mb][nb][v] + bj;
-          if (p.relu) val = val > 0.0f ? val : 0.0f;
-          yp[static_cast<int64_t>(ro) * out] = val;
-        }
-      }
+    jj[nb] = jbase + nb * DIM + ln;
+    bj[nb] = 0.0f;
+    if (p.bias != nullptr && jj[nb] < out) {
+      const float nz = noise_of_state(state_of(s, static_cast<uint64_t>(p.offset + out * in + jj[nb])));
+      bj[nb] = __builtin_fmaf(p.sigma, nz, p.bias[jj[nb]]);
     }
   }
+  store_outputs<MF, DIM>(m0 + MB * DIM <= batch, p.relu, p.y, i * batch + m0 + rb, batch - (m0 + rb), out, jj, bj,
+                            acc);
 }
 
 // WAVES: waves per SIMD the register allocation must allow; WPG: waves per
@@ -991,30 +1009,19 @@ __global__ __launch_bounds__(512, 1) void forward_rows_kernel(FwdParams p, int64
   // Epilogue: bias b_j + sigma nb_i[j] with nb at offset + out*in + j.
   if (!live) return;
   const int rb = MF::row_base(lane);
+  int64_t jj[NB];
+  float bj[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int64_t j = j0 + nb * 32 + ln;
-    if (j >= out) continue;
-    float bj = 0.0f;
-    if (p.bias != nullptr) {
-      const float nz = noise_of_state(state_of(s, static_cast<uint64_t>(p.offset + out * in + j)));
-      bj = __builtin_fmaf(p.sigma, nz, p.bias[j]);
-    }
-#pragma unroll
-    for (int mb = 0; mb < MBW; ++mb) {
-      const int64_t row0 = m0 + mb * 32 + rb;
-      float* __restrict__ yp = p.y + (i * batch + row0) * out + j;
-#pragma unroll
-      for (int v = 0; v < MF::NACC; ++v) {
-        const int ro = MF::row_off(v);
-        if (row0 + ro < batch) {
-          float val = acc[mb][nb][v] + bj;
-          if (p.relu) val = val > 0.0f ? val : 0.0f;
-          yp[static_cast<int64_t>(ro) * out] = val;
-        }
-      }
+    jj[nb] = j0 + nb * 32 + ln;
+    bj[nb] = 0.0f;
+    if (p.bias != nullptr && jj[nb] < out) {
+      const float nz = noise_of_state(state_of(s, static_cast<uint64_t>(p.offset + out * in + jj[nb])));
+      bj[nb] = __builtin_fmaf(p.sigma, nz, p.bias[jj[nb]]);
     }
   }
+  store_outputs<MF, 32>(m0 + MBW * 32 <= batch, p.relu, p.y, i * batch + m0 + rb, batch - (m0 + rb), out, jj, bj,
+                            acc);
 }
 
 template <typename IN_T, bool SPLIT>
