@@ -127,8 +127,6 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// One tile's operand sources: tile-relative row limits clamp the loads of a
-// ragged last tile to its last valid row (those rows feed discarded outputs).
 // One tile's operand sources.  The tile owns output rows [m0, m0 + 256) and
 // columns [n0, n0 + 256) (cut at batch and out); it computes rows from me and
 // columns from ne, which differ from m0 and n0 only for a ragged last tile.
