@@ -135,8 +135,8 @@ int vn_compute_offsets(const int64_t* dims, const int32_t* ndims, int32_t n_bloc
  *   workspace     DEVICE scratch of workspace_bytes (16-byte aligned), or NULL
  *                 with workspace_bytes 0.  When it holds at least
  *                 vn_perturbed_linear_workspace_size bytes for these sizes (bf16
- *                 operands and many rows per individual; 16-byte aligned x and
- *                 w), the perturbed weights of groups of individuals are formed
+ *                 operands, many rows per individual, at least 256 outputs;
+ *                 16-byte aligned x and w), the perturbed weights of groups of individuals are formed
  *                 there once and multiplied on the matrix cores; otherwise the
  *                 noise is generated inside the product.  Both give the same
  *                 bits.  The library only reads what it wrote there during the
