@@ -108,6 +108,9 @@ def parse():
                     help="approximate CPU seconds for the oracle baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (to scale memory counters)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time the vendor bf16 GEMM (torch linear -> hipBLASLt) on the large-batch "
+                         "workload's products, for context beside the materialized path")
     ap.add_argument("--fused-chain", action="store_true",
                     help="run a multi-layer workload's forward through the fused chain entry point")
     ap.add_argument("--only", choices=["forward", "gradient", "metric"], default=None,
@@ -278,6 +281,37 @@ def copy_calibration(torch, device):
                       "launches": 3}))
 
 
+def vendor_gemm(torch, device, workload, steps):
+    """The vendor GEMM on the products the large-batch workload's materialized
+    path computes: Y_g = X W_g^T (bf16 operands and output) for 8 weight
+    matrices of the workload's shape, back to back; a reference point for the
+    matrix-core kernel, not part of the hot path."""
+    L = workload.layers[0]
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    x = torch.randn((workload.batch, L.in_features), generator=gen).to(torch.bfloat16).to(device)
+    ws = [torch.randn((L.out_features, L.in_features), generator=gen).to(torch.bfloat16).to(device) for _ in range(8)]
+    for _ in range(3):
+        for w in ws:
+            torch.nn.functional.linear(x, w)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for w in ws:
+            torch.nn.functional.linear(x, w)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    ms = times[len(times) // 2]
+    flops = 8 * 2.0 * workload.batch * L.in_features * L.out_features
+    print(json.dumps({"vendor_gemm": "torch.nn.functional.linear, bf16, 8 products", "batch": workload.batch,
+                      "in": L.in_features, "out": L.out_features, "ms_per_8_products": round(ms, 4),
+                      "tflops": round(flops / ms / 1e9, 1), "frac_of_bf16_peak": round(flops / ms / 1e9 / 2500, 4),
+                      "steps": steps}))
+
+
 def flops_of(wl) -> float:
     return float(sum(2.0 * wl.pop * wl.batch * L.in_features * L.out_features for L in wl.layers))
 
@@ -431,6 +465,9 @@ def main():
     device = torch.device("cuda:0")
     if args.copy_calibration:
         copy_calibration(torch, device)
+        return
+    if args.vendor_gemm:
+        vendor_gemm(torch, device, workloads.make(6), max(args.steps // 5, 5))
         return
     wl = workloads.make(args.workload)
     step = Step(wl, torch, vn, device, fused=args.fused_chain)
