@@ -73,6 +73,28 @@ def test_materialized_against_oracle(pop, batch, fin, fout, offset):
     assert_close(y, ref, TOL_BF16, "materialized forward")
 
 
+@pytest.mark.parametrize("fout", [255, 256])
+def test_output_width_boundary(fout):
+    """Fewer than 256 outputs keep the noise inside the product (no workspace);
+    256 take the materialized path.  Both against the oracle, and the
+    materialized result against the fused one bit for bit."""
+    pop, batch, fin, offset = 1, 2048, 128, 77
+    print(f"output width {fout}", flush=True)
+    ws = _ws_bytes(pop, batch, fin, fout)
+    assert (ws > 0) == (fout >= 256)
+    wl = workloads.make_custom(pop, batch, fin, fout, dtype="bf16", bias=True, shared_x=False, sigma=0.05,
+                               offset=offset, seed=fout)
+    L = wl.layers[0]
+    args = (to_dev(wl.x, torch.bfloat16), to_dev(L.weight, torch.bfloat16), to_dev(L.bias), to_dev(wl.seeds),
+            wl.sigma, offset)
+    ym = vn.virtual_perturbed_linear(*args, materialize=True)
+    yf = vn.virtual_perturbed_linear(*args, materialize=False)
+    torch.cuda.synchronize()
+    assert torch.equal(ym, yf)
+    ref = oracle.perturbed_linear(wl.x, L.weight, L.bias, wl.seeds, sigma32(wl.sigma), offset)
+    assert_close(ym.cpu().numpy(), ref, TOL_BF16, f"forward, {fout} outputs")
+
+
 def test_materialized_several_groups():
     """4096 x 4096 weights: 8 individuals per 256 MiB group, so 9 individuals
     take two groups (the second with one individual)."""
